@@ -1,0 +1,193 @@
+"""fp8 e4m3 latent KV cache for MLA decode on MI355X (gfx950).
+
+Thin Python binding of libkv8.so (include/kv8.h): it checks tensor dtypes,
+devices, shapes and contiguity, passes raw device pointers and the current
+HIP stream, and raises on a nonzero status.  Every step of the computation
+runs in the HIP kernels; there is no fallback path.  PyTorch only provides
+device memory and streams.
+
+Cache layout: codes uint8 [rows, 576] (512 Lc codes, then 64 Rc codes),
+scales float32 [rows, 2] (Lc scale, Rc scale).  bf16 queries are passed as
+torch.bfloat16 tensors.
+"""
+import ctypes
+import os
+
+KV_LORA = 512
+ROPE = 64
+ROW_BYTES = KV_LORA + ROPE
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkv8.so")
+
+_STATUS = {0: "KV8_OK", -1: "KV8_EINVAL", -2: "KV8_EUNSUPPORTED", -3: "KV8_ELAUNCH",
+           -4: "KV8_EWORKSPACE", -5: "KV8_ENOMEM"}
+
+# every symbol include/kv8.h declares
+EXPORTS = ("kv8_quantize_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
+           "kv8_absorb_decode_splitT", "kv8_status_string", "kv8_encode_bits",
+           "kv8_decode_codes")
+
+_lib = None
+
+
+class Kv8Error(RuntimeError):
+    def __init__(self, fn, status):
+        msg = lib().kv8_status_string(status).decode()
+        super().__init__("%s failed: %s (%s)" % (fn, _STATUS.get(status, status), msg))
+        self.status = status
+
+
+def lib():
+    """Load libkv8.so.  It must have been built (python -m fp8_e4m3_latent_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libkv8.so is not built: run `python -m fp8_e4m3_latent_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32, u64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                       ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t,
+                                       ctypes.c_float)
+    L.kv8_status_string.restype = ctypes.c_char_p
+    L.kv8_status_string.argtypes = [ctypes.c_int]
+    L.kv8_quantize_rows.restype = ctypes.c_int
+    L.kv8_quantize_rows.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+    dec = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+    L.kv8_absorb_decode.restype = ctypes.c_int
+    L.kv8_absorb_decode.argtypes = dec + [vp]
+    L.kv8_splitT_workspace_bytes.restype = sz
+    L.kv8_splitT_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.kv8_absorb_decode_splitT.restype = ctypes.c_int
+    L.kv8_absorb_decode_splitT.argtypes = dec + [i32, vp, sz, vp]
+    L.kv8_encode_bits.restype = ctypes.c_int
+    L.kv8_encode_bits.argtypes = [u32, u64, vp, vp]
+    L.kv8_decode_codes.restype = ctypes.c_int
+    L.kv8_decode_codes.argtypes = [vp, i64, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, ndim=None, contiguous=True):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor, got %s" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %s" % (name, ndim, tuple(t.shape)))
+    if contiguous and not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _call(fn, *args):
+    rc = getattr(lib(), fn)(*args)
+    if rc != 0:
+        raise Kv8Error(fn, rc)
+
+
+def quantize_rows(src, codes, scales, dst_rows=None, stream=None):
+    """Quantize f32 token rows src [n, >=576] (row stride may exceed 576) into
+    the cache: row i -> cache row dst_rows[i] (int64 GPU tensor) or i."""
+    torch = _torch()
+    _check(src, "src", torch.float32, 2, contiguous=False)
+    if src.stride(1) != 1:
+        raise ValueError("src rows must be contiguous")
+    if src.shape[1] < ROW_BYTES:
+        raise ValueError("src rows must hold at least %d values" % ROW_BYTES)
+    pc = _check(codes, "codes", torch.uint8, 2)
+    ps = _check(scales, "scales", torch.float32, 2)
+    if codes.shape[1] != ROW_BYTES or scales.shape[1] != 2 or scales.shape[0] != codes.shape[0]:
+        raise ValueError("cache must be codes [rows, 576] uint8 and scales [rows, 2] f32")
+    pd = None
+    if dst_rows is not None:
+        pd = _check(dst_rows, "dst_rows", torch.int64, 1)
+        if dst_rows.numel() != src.shape[0]:
+            raise ValueError("dst_rows must have one entry per source row")
+    elif src.shape[0] > codes.shape[0]:
+        raise ValueError("cache has fewer rows than src")
+    _call("kv8_quantize_rows", ctypes.c_void_p(src.data_ptr()), src.stride(0), src.shape[0],
+          KV_LORA, ROPE, pc, ps, pd, _stream(stream))
+
+
+def _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out):
+    torch = _torch()
+    pql = _check(q_lat, "q_lat", torch.bfloat16, 4)
+    pqr = _check(q_rope, "q_rope", torch.bfloat16, 4)
+    B, Q, H, kl = q_lat.shape
+    if kl != KV_LORA or tuple(q_rope.shape) != (B, Q, H, ROPE):
+        raise ValueError("q_lat must be [B,Q,H,512] and q_rope [B,Q,H,64]")
+    pc = _check(codes, "codes", torch.uint8, 2)
+    ps = _check(scales, "scales", torch.float32, 2)
+    pst = _check(kv_start, "kv_start", torch.int64, 1)
+    pln = _check(kv_len, "kv_len", torch.int32, 1)
+    if kv_start.numel() != B or kv_len.numel() != B:
+        raise ValueError("kv_start and kv_len need one entry per sequence")
+    if out is None:
+        out = torch.empty((B, Q, H, KV_LORA), dtype=torch.float32, device=q_lat.device)
+    po = _check(out, "out", torch.float32, 4)
+    if tuple(out.shape) != (B, Q, H, KV_LORA):
+        raise ValueError("out must be [B,Q,H,512]")
+    return [pql, pqr, pc, ps, pst, pln, int(max_len), B, Q, H, KV_LORA, ROPE], out, po
+
+
+def absorb_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, softmax_scale,
+                  out=None, stream=None):
+    """Absorbed-MLA decode over the fp8 cache; returns out f32 [B,Q,H,512]."""
+    args, out, po = _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out)
+    _call("kv8_absorb_decode", *args, ctypes.c_float(softmax_scale), po, _stream(stream))
+    return out
+
+
+def splitT_workspace_bytes(B, Q, H, num_splits):
+    return int(lib().kv8_splitT_workspace_bytes(B, Q, H, KV_LORA, num_splits))
+
+
+def absorb_decode_splitT(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len,
+                         softmax_scale, num_splits, workspace=None, out=None, stream=None):
+    """Split-T decode with num_splits equal token ranges per sequence merged by
+    log-sum-exp.  workspace: uint8 GPU tensor of splitT_workspace_bytes()."""
+    torch = _torch()
+    args, out, po = _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out)
+    B, Q, H = args[7], args[8], args[9]
+    need = splitT_workspace_bytes(B, Q, H, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    pw = _check(workspace, "workspace", torch.uint8, 1)
+    _call("kv8_absorb_decode_splitT", *args, ctypes.c_float(softmax_scale), po,
+          int(num_splits), pw, workspace.numel(), _stream(stream))
+    return out
+
+
+def encode_bits(first, count, out, stream=None):
+    """out[k] = device encoder's code of the f32 with bit pattern first + k."""
+    torch = _torch()
+    po = _check(out, "out", torch.uint8, 1)
+    if out.numel() < count:
+        raise ValueError("out too small")
+    _call("kv8_encode_bits", ctypes.c_uint32(first), ctypes.c_uint64(count), po, _stream(stream))
+
+
+def decode_codes(codes, stream=None):
+    """(bf16 bits, fp16 bits) of the device decode of every code (int16 tensors)."""
+    torch = _torch()
+    pc = _check(codes, "codes", torch.uint8, 1)
+    bf = torch.empty(codes.numel(), dtype=torch.int16, device=codes.device)
+    hf = torch.empty(codes.numel(), dtype=torch.int16, device=codes.device)
+    _call("kv8_decode_codes", pc, codes.numel(), ctypes.c_void_p(bf.data_ptr()),
+          ctypes.c_void_p(hf.data_ptr()), _stream(stream))
+    return bf, hf

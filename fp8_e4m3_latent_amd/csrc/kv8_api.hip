@@ -1,0 +1,188 @@
+// C ABI of libkv8 (declared in include/kv8.h): argument checks and launches.
+// No call allocates except kv8_absorb_decode's stream-ordered split partials,
+// none synchronizes the host, none prints or aborts.
+#include "kv8.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kv8_internal.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launched(int rc) { return rc == 0 ? KV8_OK : KV8_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kv8_status_string(int status) {
+    switch (status) {
+        case KV8_OK: return "ok";
+        case KV8_EINVAL: return "invalid argument";
+        case KV8_EUNSUPPORTED: return "unsupported shape (kv_lora must be 512, rope 64)";
+        case KV8_ELAUNCH: return "HIP launch failed";
+        case KV8_EWORKSPACE: return "split-T workspace missing or too small";
+        case KV8_ENOMEM: return "device allocation of split partials failed";
+        default: return "unknown kv8 status";
+    }
+}
+
+int kv8_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows, int32_t kv_lora,
+                      int32_t rope, uint8_t* codes, float* scales, const int64_t* dst_rows,
+                      void* stream) {
+    if (n_rows < 0) return KV8_EINVAL;
+    if (kv_lora != kv8::kKvLora || rope != kv8::kRope) return KV8_EUNSUPPORTED;
+    if (n_rows == 0) return KV8_OK;
+    if (!src || !codes || !scales) return KV8_EINVAL;
+    if (src_row_stride < kv_lora + rope || src_row_stride % 4 != 0) return KV8_EINVAL;
+    if (!aligned(src, 16) || !aligned(codes, 4) || !aligned(scales, 8)) return KV8_EINVAL;
+    if (dst_rows && !aligned(dst_rows, 8)) return KV8_EINVAL;
+    return launched(kv8::launch_quantize_rows(src, src_row_stride, n_rows, codes, scales, dst_rows,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int kv8_encode_bits(uint32_t first, uint64_t count, uint8_t* out, void* stream) {
+    if (count == 0) return KV8_OK;
+    if (!out || !aligned(out, 4)) return KV8_EINVAL;
+    if (count > (uint64_t(1) << 32) - first) return KV8_EINVAL;
+    return launched(kv8::launch_encode_bits(first, count, out, static_cast<hipStream_t>(stream)));
+}
+
+int kv8_decode_codes(const uint8_t* codes, int64_t n, uint16_t* out_bf16, uint16_t* out_f16,
+                     void* stream) {
+    if (n < 0) return KV8_EINVAL;
+    if (n == 0) return KV8_OK;
+    if (!codes || !out_bf16 || !out_f16) return KV8_EINVAL;
+    return launched(kv8::launch_decode_codes(codes, n, out_bf16, out_f16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Absorbed decode
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kRowsPerBlock = 128;   // query rows per decode block
+constexpr int kTargetBlocks = 256;   // one block per compute unit
+
+int64_t row_blocks(int32_t Q, int32_t H) {
+    return (static_cast<int64_t>(Q) * H + kRowsPerBlock - 1) / kRowsPerBlock;
+}
+
+int check_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,
+                 const float* scales, const int64_t* kv_start, const int32_t* kv_len,
+                 int32_t max_len, int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                 float softmax_scale, const float* out) {
+    if (B < 1 || Q < 1 || H < 1 || max_len < 0) return KV8_EINVAL;
+    if (kv_lora != kv8::kKvLora || rope != kv8::kRope) return KV8_EUNSUPPORTED;
+    if (!q_lat || !q_rope || !codes || !scales || !kv_start || !kv_len || !out) return KV8_EINVAL;
+    if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
+        softmax_scale == -INFINITY)
+        return KV8_EINVAL;
+    if (!aligned(q_lat, 16) || !aligned(q_rope, 16) || !aligned(codes, 16) ||
+        !aligned(scales, 8) || !aligned(kv_start, 8) || !aligned(kv_len, 4) || !aligned(out, 16))
+        return KV8_EINVAL;
+    const int64_t blocks = static_cast<int64_t>(B) * row_blocks(Q, H);
+    if (blocks > (int64_t(1) << 30) || static_cast<int64_t>(Q) * H > (int64_t(1) << 24))
+        return KV8_EUNSUPPORTED;
+    return KV8_OK;
+}
+
+// sub-ranges per requested split so that the grid reaches one block per CU
+int sub_splits(int32_t B, int32_t Q, int32_t H, int32_t num_splits) {
+    const int64_t units = static_cast<int64_t>(B) * row_blocks(Q, H) * num_splits;
+    const int64_t sub = units >= kTargetBlocks ? 1 : kTargetBlocks / units;
+    return static_cast<int>(sub < 1 ? 1 : sub);
+}
+
+kv8::DecodeLaunch make_launch(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,
+                              const float* scales, const int64_t* kv_start,
+                              const int32_t* kv_len, int32_t B, int32_t Q, int32_t H,
+                              float softmax_scale, float* out) {
+    kv8::DecodeLaunch d{};
+    d.q_lat = q_lat;
+    d.q_rope = q_rope;
+    d.codes = codes;
+    d.scales = scales;
+    d.kv_start = kv_start;
+    d.kv_len = kv_len;
+    d.B = B;
+    d.Q = Q;
+    d.H = H;
+    // a zero scale would turn masked scores into 0 * inf; the smallest normal
+    // scale gives the same (uniform) softmax
+    d.softmax_scale = softmax_scale == 0.0f ? 1.17549435e-38f : softmax_scale;
+    d.out = out;
+    d.n_splits = 1;
+    d.split_chunk = 0;
+    d.n_sub = 1;
+    d.workspace = nullptr;
+    return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kv8_splitT_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                                  int32_t num_splits) {
+    if (B < 1 || Q < 1 || H < 1 || num_splits < 1 || kv_lora != kv8::kKvLora) return 0;
+    const int total = num_splits * sub_splits(B, Q, H, num_splits);
+    return total > 1 ? kv8::splitT_workspace_bytes(B, Q, H, total) : 0;
+}
+
+int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,
+                      const float* scales, const int64_t* kv_start, const int32_t* kv_len,
+                      int32_t max_len, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                      int32_t rope, float softmax_scale, float* out, void* stream) {
+    int rc = check_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, B, Q, H,
+                          kv_lora, rope, softmax_scale, out);
+    if (rc != KV8_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    kv8::DecodeLaunch d =
+        make_launch(q_lat, q_rope, codes, scales, kv_start, kv_len, B, Q, H, softmax_scale, out);
+    // token ranges of a fixed size (a multiple of the 32-token tile) so that
+    // B x row blocks x ranges fills the compute units
+    const int64_t units = static_cast<int64_t>(B) * row_blocks(Q, H);
+    int64_t splits = (kTargetBlocks + units - 1) / units;
+    const int64_t by_len = (static_cast<int64_t>(max_len) + 1023) / 1024;
+    splits = splits < by_len ? splits : by_len;
+    if (splits <= 1) return launched(kv8::launch_absorb_decode(d, st));
+    int64_t chunk = (max_len + splits - 1) / splits;
+    chunk = (chunk + 31) / 32 * 32;
+    splits = (max_len + chunk - 1) / chunk;
+    d.n_splits = static_cast<int>(splits);
+    d.split_chunk = static_cast<int>(chunk);
+    const size_t bytes = kv8::splitT_workspace_bytes(B, Q, H, d.n_splits);
+    if (hipMallocAsync(&d.workspace, bytes, st) != hipSuccess) return KV8_ENOMEM;
+    rc = launched(kv8::launch_absorb_decode(d, st));
+    if (hipFreeAsync(d.workspace, st) != hipSuccess && rc == KV8_OK) rc = KV8_ELAUNCH;
+    return rc;
+}
+
+int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,
+                             const float* scales, const int64_t* kv_start, const int32_t* kv_len,
+                             int32_t max_len, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                             int32_t rope, float softmax_scale, float* out, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, B, Q, H,
+                          kv_lora, rope, softmax_scale, out);
+    if (rc != KV8_OK) return rc;
+    if (num_splits < 1 || num_splits > (1 << 20)) return KV8_EINVAL;
+    kv8::DecodeLaunch d =
+        make_launch(q_lat, q_rope, codes, scales, kv_start, kv_len, B, Q, H, softmax_scale, out);
+    d.n_sub = sub_splits(B, Q, H, num_splits);
+    d.n_splits = num_splits * d.n_sub;
+    if (d.n_splits > 1) {
+        const size_t need = kv8::splitT_workspace_bytes(B, Q, H, d.n_splits);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KV8_EWORKSPACE;
+        d.workspace = workspace;
+    }
+    return launched(kv8::launch_absorb_decode(d, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

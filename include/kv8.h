@@ -1,0 +1,156 @@
+/* kv8 -- fp8 e4m3 latent KV cache for multi-head latent attention on MI355X.
+ *
+ * C ABI of libkv8.so (hand-written HIP for gfx950).  The operations follow
+ * the page "KV8=1: fp8 e4m3 latent KV cache (CPU + CUDA) with .coli_kv v2"
+ * (colibri pull request #299), cited below as [colibri#299]:
+ *
+ *   commit message, first paragraph: the MLA latent rows -- Lc (kv_lora) and
+ *     Rc (qk_rope) -- are stored as fp8 e4m3 bytes with a per-row f32
+ *     amax/448 scale; the latent is both key and value of the absorbed
+ *     attention.
+ *   commit message, kv_fp8.h item: round-to-nearest-even encoder saturating
+ *     at +-448, keeping the sign of zero and storing NaN as an inert 0; the
+ *     per-row quantizer guards an amax so small that 448/amax overflows.
+ *   commit message, attention_rows item: the producer quantizes each fresh
+ *     row instead of copying f32; the absorbed score and context loops
+ *     dequantize inline with the row scale applied outside the dot product.
+ *   PR description: one f32 scale each for the Lc and the Rc row; a follow-up
+ *     adds split-T kernels for long slots.
+ *
+ * Element format: OCP 8-bit floating point, E4M3 (bias 7, no infinities,
+ * NaN = S.1111.111, largest finite 448, subnormals m * 2^-9).
+ *
+ * Cache layout (device memory, owned by the caller):
+ *   codes  uint8 [n_cache_rows][kv_lora + rope], row-major, one token row per
+ *          cache row: the kv_lora Lc codes, then the rope Rc codes;
+ *   scales f32   [n_cache_rows][2]: scales[r][0] for Lc, scales[r][1] for Rc.
+ *   A token occupies kv_lora + rope + 8 bytes per layer (584 for 512 + 64).
+ *
+ * Conventions for every call:
+ *   - every pointer argument is a DEVICE pointer owned by the caller, except
+ *     where stated; buffers must stay valid until the stream has finished;
+ *   - `stream` is a hipStream_t (NULL = the default stream); calls are
+ *     asynchronous on it and never synchronize the host;
+ *   - bf16 values are passed as their uint16_t bit patterns;
+ *   - the library keeps no state between calls; kv8_absorb_decode may take
+ *     stream-ordered device memory (hipMallocAsync) for split partials and
+ *     returns it on the same stream before returning;
+ *   - argument errors are reported synchronously through the return value
+ *     and nothing is launched; data is never an error (NaN, inf, zero and
+ *     subnormal values have defined results); nothing aborts or prints.
+ *
+ * Supported shapes: kv_lora = 512, rope = 64 (other values return
+ * KV8_EUNSUPPORTED).
+ */
+#ifndef KV8_H
+#define KV8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KV8_OK = 0,
+    KV8_EINVAL = -1,        /* bad argument: null pointer, negative size, bad alignment */
+    KV8_EUNSUPPORTED = -2,  /* valid but unsupported shape (kv_lora != 512, rope != 64) */
+    KV8_ELAUNCH = -3,       /* a HIP launch or runtime call failed */
+    KV8_EWORKSPACE = -4,    /* split-T workspace missing or too small */
+    KV8_ENOMEM = -5         /* stream-ordered allocation of split partials failed */
+} kv8_status;
+
+/* Quantize f32 latent token rows into the fp8 cache ([colibri#299] commit
+ * message, kv_fp8.h and attention_rows items; PR description).
+ *
+ * src            f32 [n_rows][src_row_stride]; row i holds kv_lora Lc values
+ *                then rope Rc values (further columns are ignored).  src must
+ *                be 16-byte aligned and src_row_stride a multiple of 4,
+ *                >= kv_lora + rope.
+ * n_rows         rows to quantize (0 is a no-op).
+ * codes, scales  the cache (layout above); row i is written to cache row
+ *                dst_rows[i], or to row i when dst_rows is NULL.  codes must
+ *                be 4-byte and scales 8-byte aligned.
+ * dst_rows       int64 [n_rows] device array or NULL.  Rows must be distinct
+ *                and inside the cache (not checked: they are device data).
+ *
+ * Per segment x (Lc, then Rc): amax = max |x_j| over finite entries (0 if
+ * none); inv = fl32(448 / amax); if inv is +inf the segment is guarded:
+ * scale = +0 and inv = 0; otherwise scale = fl32(amax / 448).  Each code is
+ * the saturating round-to-nearest-even e4m3 encoding of fl32(x_j * inv):
+ * |q| >= 448 (and +-inf) -> +-448 (0x7E | sign), sign of zero kept, NaN ->
+ * 0x00.  Results are bit-identical to this definition. */
+int kv8_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
+                      int32_t kv_lora, int32_t rope,
+                      uint8_t* codes, float* scales, const int64_t* dst_rows,
+                      void* stream);
+
+/* Absorbed-MLA decode straight from the fp8 rows ([colibri#299] commit
+ * message, first paragraph and attention_rows item).
+ *
+ * q_lat          bf16 [B][Q][H][kv_lora]  (queries already absorbed into the
+ *                latent space), 16-byte aligned.
+ * q_rope         bf16 [B][Q][H][rope], 16-byte aligned.
+ * codes, scales  the cache; codes 16-byte aligned.
+ * kv_start       int64 [B]: first cache row of sequence b.
+ * kv_len         int32 [B]: rows of sequence b, including its Q newest ones;
+ *                0 <= kv_len[b] <= max_len.
+ * max_len        host-side upper bound of kv_len (sizes the launch).
+ * B, Q, H        sequences, query positions per sequence, heads (>= 1).
+ * softmax_scale  f32 multiplier of the scores (e.g. 1/sqrt(576)).
+ * out            f32 [B][Q][H][kv_lora], 16-byte aligned: the normalised
+ *                latent context (before any value up-projection).
+ *
+ * Query i of sequence b attends its first n = kv_len[b] - (Q-1) + i rows
+ * (causal multi-token decode); n <= 0 gives a zero output.  For every
+ * visible row t: s_t = softmax_scale * (scale_Lc[t] * (q_lat . dec(Lc_t)) +
+ * scale_Rc[t] * (q_rope . dec(Rc_t))); out = sum_t softmax(s)_t *
+ * scale_Lc[t] * dec(Lc_t).  Long sequences are split internally and merged
+ * by log-sum-exp. */
+int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope,
+                      const uint8_t* codes, const float* scales,
+                      const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
+                      int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                      float softmax_scale, float* out, void* stream);
+
+/* Bytes of workspace kv8_absorb_decode_splitT needs for these shapes. */
+size_t kv8_splitT_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                                  int32_t num_splits);
+
+/* Split-T decode ([colibri#299] PR description, follow-up paragraph: split-T
+ * kernels for long slots).  Same arguments and result as kv8_absorb_decode;
+ * the rows [0, kv_len[b]) of every sequence are cut into num_splits equal
+ * ranges of ceil(kv_len[b] / num_splits) rows (the last ones may be short or
+ * empty), each range yields a partial softmax (running max, sum, weighted
+ * context), and the partials are merged by log-sum-exp.  workspace is a
+ * caller-owned device buffer of at least
+ * kv8_splitT_workspace_bytes(B, Q, H, kv_lora, num_splits) bytes, 256-byte
+ * aligned; its contents on entry do not matter. */
+int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope,
+                             const uint8_t* codes, const float* scales,
+                             const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
+                             int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                             float softmax_scale, float* out,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Human-readable name of a kv8_status value (static string, never NULL). */
+const char* kv8_status_string(int status);
+
+/* ---- Verification entry points (same device code as the calls above) ---- */
+
+/* out[k] = e4m3 code of the f32 value whose bit pattern is first + k, for
+ * k < count (count <= 2^32 - first), with the encoder kv8_quantize_rows uses.
+ * out must be 4-byte aligned. */
+int kv8_encode_bits(uint32_t first, uint64_t count, uint8_t* out, void* stream);
+
+/* Decode n codes with the exact conversions the decode kernels use:
+ * out_bf16[k], out_f16[k] = bit patterns of dec(codes[k]) as bf16 and fp16. */
+int kv8_decode_codes(const uint8_t* codes, int64_t n, uint16_t* out_bf16, uint16_t* out_f16,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KV8_H */

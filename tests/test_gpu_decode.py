@@ -1,0 +1,211 @@
+"""GPU parity of kv8_absorb_decode / kv8_absorb_decode_splitT against the oracle.
+
+The cache is built by the GPU quantizer and checked bit-exact against the
+oracle's codes first; both sides then decode the SAME codes, scales and bf16
+queries (the kernel is compared with a host reference on the dequantized
+cache, not with unquantized attention).  Bar: max|gpu - oracle| /
+max|oracle| <= 1e-3 over every compared output row.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_e4m3_latent_amd import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+KL, KR, D = 512, 64, 576
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def kv8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_e4m3_latent_amd as m
+    m.lib()
+    return m
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def build_cache(kv8, rows, check=True):
+    """GPU-quantize rows into a device cache; optionally check bit-exactness."""
+    n = rows.shape[0]
+    src = torch.from_numpy(np.ascontiguousarray(rows)).cuda()
+    codes = torch.empty((max(n, 1), D), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((max(n, 1), 2), dtype=torch.float32, device="cuda")
+    kv8.quantize_rows(src, codes, scales)
+    torch.cuda.synchronize()
+    del src
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    if check and n:
+        rc, rs = oracle.quantize_rows(rows)
+        assert np.array_equal(c[:n], rc), "quantized codes differ from the oracle"
+        assert np.array_equal(s[:n].view(np.uint32), rs.view(np.uint32)), "scales differ"
+    return codes, scales, c, s
+
+
+def to_dev(w):
+    ql = torch.from_numpy(w.q_lat.view(np.int16)).cuda().view(torch.bfloat16)
+    qr = torch.from_numpy(w.q_rope.view(np.int16)).cuda().view(torch.bfloat16)
+    st = torch.from_numpy(w.kv_start.astype(np.int64)).cuda()
+    ln = torch.from_numpy(w.kv_len.astype(np.int32)).cuda()
+    return ql, qr, st, ln
+
+
+def rel_err(got, ref):
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def run_case(kv8, w, splits=None, sel=None, check_cache=True, cache=None):
+    say("decode: %s B=%d Q=%d H=%d max_len=%d splits=%s" % (
+        w.name, w.B, w.Q, w.H, w.max_len, splits))
+    codes, scales, c, s = cache if cache is not None else build_cache(kv8, w.rows, check_cache)
+    ql, qr, st, ln = to_dev(w)
+    if splits is None:
+        out = kv8.absorb_decode(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale)
+    else:
+        out = kv8.absorb_decode_splitT(ql, qr, codes, scales, st, ln, w.max_len,
+                                       w.softmax_scale, splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1, KL)
+    ref = oracle.attention(w.q_lat, w.q_rope, c, s, w.kv_start, w.kv_len, Q=w.Q,
+                           softmax_scale=w.softmax_scale, sel=sel)
+    if sel is not None:
+        got = got[sel]
+    ref = ref.reshape(-1, KL)
+    assert np.all(np.isfinite(got))
+    e = rel_err(got, ref)
+    say("  max|d|/max|ref| = %.3g" % e)
+    assert e <= TOL, e
+    return got, ref
+
+
+def test_tiny_workload(kv8):
+    """B=1, H=16, T=1024, outlier rows (x50), every output row."""
+    run_case(kv8, workloads.tiny(seed=0))
+
+
+def test_ragged_causal_multi_query_small(kv8):
+    """Q=4 causal queries, H=128 (four 128-row blocks), lengths with ragged tails."""
+    w = workloads.batched(seed=1, B=3, T=1, H=128, Q=4)
+    rng = np.random.default_rng(2)
+    lens = np.array([37, 1000, 300], np.int32)
+    w.kv_len = lens
+    w.kv_start = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    w.rows = rng.standard_normal((int(lens.sum()), D)).astype(np.float32)
+    w.name = "ragged-small"
+    run_case(kv8, w)
+
+
+def test_heads_not_multiple_of_block(kv8):
+    """Q*H = 48 rows: one partly filled row block."""
+    w = workloads.tiny(seed=3, B=2, Q=3, H=16, T=333)
+    run_case(kv8, w)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7, 64])
+def test_splitT_small(kv8, splits):
+    w = workloads.tiny(seed=4, B=2, Q=1, H=128, T=5000, outlier_p=0.0)
+    run_case(kv8, w, splits=splits)
+
+
+def test_empty_and_short_sequences(kv8):
+    """kv_len 0 -> zeros; kv_len 2 with Q=4 -> the first two queries see nothing."""
+    w = workloads.tiny(seed=5, B=3, Q=4, H=16, T=40)
+    w.kv_len = np.array([0, 2, 40], np.int32)
+    w.kv_start = np.array([0, 0, 40], np.int64)
+    got, ref = run_case(kv8, w)
+    got = got.reshape(3, 4, 16, KL)
+    assert not got[0].any() and not got[1, :2].any() and got[1, 2:].any()
+
+
+def test_extreme_row_scales(kv8):
+    """Sequences whose rows have amax near 1e-30, 1 and 1e30 (scales far outside
+    the fp16 range of the probabilities), and inside one sequence guarded
+    (all-zero) rows next to rows a thousand times larger than the rest."""
+    w = workloads.tiny(seed=6, B=3, Q=1, H=32, T=200, outlier_p=0.0)
+    mult = np.array([1e-30, 1.0, 1e30], np.float32)
+    for b in range(3):
+        w.rows[b * 200:(b + 1) * 200] *= mult[b]
+    w.rows[210:215] = 0.0
+    w.rows[220] *= np.float32(1e3)
+    w.rows[390] *= np.float32(1e3)
+    run_case(kv8, w)
+
+
+def test_reference_raise_restart(kv8):
+    """A late tile scores ~20 natural-log units above the first tiles, forcing
+    the block to raise its reference maximum and run its range again."""
+    w = workloads.tiny(seed=7, B=1, Q=1, H=32, T=900, outlier_p=0.0)
+    ql = workloads.bf16_to_f32(w.q_lat[0, 0])
+    unit = ql / np.linalg.norm(ql, axis=1, keepdims=True)
+    for k, t in enumerate([700, 701, 850]):
+        h = k % 32
+        # score = (1/24) * q_h . Lc_t = 20 (natural-log units) for head h
+        w.rows[t, :KL] = (20.0 * 24.0 / np.linalg.norm(ql[h])) * unit[h]
+    run_case(kv8, w)
+
+
+def test_negative_and_zero_softmax_scale(kv8):
+    w = workloads.tiny(seed=8, B=2, Q=2, H=16, T=300)
+    w.softmax_scale = np.float32(-1.0 / 24.0)
+    run_case(kv8, w)
+    w.softmax_scale = np.float32(0.0)
+    run_case(kv8, w)
+
+
+def test_deterministic(kv8):
+    w = workloads.tiny(seed=9, B=2, Q=1, H=128, T=3000)
+    codes, scales, c, s = build_cache(kv8, w.rows)
+    ql, qr, st, ln = to_dev(w)
+    a = kv8.absorb_decode(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale)
+    b = kv8.absorb_decode(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_argument_errors(kv8):
+    w = workloads.tiny(seed=10, B=1, Q=1, H=16, T=64)
+    codes, scales, c, s = build_cache(kv8, w.rows)
+    ql, qr, st, ln = to_dev(w)
+    with pytest.raises(kv8.Kv8Error):
+        kv8.absorb_decode_splitT(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale,
+                                 num_splits=0)
+    with pytest.raises(kv8.Kv8Error):
+        kv8.absorb_decode(ql, qr, codes, scales, st, ln, w.max_len, float("nan"))
+    small = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kv8.Kv8Error):
+        kv8.absorb_decode_splitT(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale,
+                                 num_splits=4, workspace=small)
+
+
+# ---------------------------------------------------------------- full sizes
+
+def sample_rows(B, Q, H, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(B * Q * H, size=min(n, B * Q * H), replace=False)).astype(np.int64)
+
+
+def test_batched_full_size_sampled(kv8):
+    """B=32, T=8192, H=128 (the bench launch), 96 sampled output rows."""
+    w = workloads.batched(seed=0)
+    run_case(kv8, w, sel=sample_rows(w.B, w.Q, w.H, 96, 11))
+
+
+def test_long_context_splitT_full_size_sampled(kv8):
+    """B=1, T=262144, H=128, 64 split ranges merged by log-sum-exp; planted
+    strong matches make the softmax peaked."""
+    w = workloads.long_context(seed=0)
+    run_case(kv8, w, splits=64, sel=sample_rows(1, 1, w.H, 24, 12))
+
+
+def test_ragged_full_size_sampled(kv8):
+    """B=64, lengths U[1k, 64k], Q=4 causal, whole cache quantized on the GPU."""
+    w = workloads.ragged(seed=0)
+    run_case(kv8, w, sel=sample_rows(w.B, w.Q, w.H, 48, 13))

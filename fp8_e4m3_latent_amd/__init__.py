@@ -25,8 +25,9 @@ _STATUS = {0: "KV8_OK", -1: "KV8_EINVAL", -2: "KV8_EUNSUPPORTED", -3: "KV8_ELAUN
 
 # every symbol include/kv8.h declares
 EXPORTS = ("kv8_quantize_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
-           "kv8_absorb_decode_splitT", "kv8_status_string", "kv8_encode_bits",
-           "kv8_decode_codes")
+           "kv8_absorb_decode_splitT", "kv8_partials_bytes", "kv8_decode_plan",
+           "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
+           "kv8_encode_bits", "kv8_decode_codes")
 
 _lib = None
 
@@ -60,6 +61,14 @@ def lib():
     L.kv8_splitT_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.kv8_absorb_decode_splitT.restype = ctypes.c_int
     L.kv8_absorb_decode_splitT.argtypes = dec + [i32, vp, sz, vp]
+    L.kv8_partials_bytes.restype = sz
+    L.kv8_partials_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.kv8_decode_plan.restype = ctypes.c_int
+    L.kv8_decode_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.kv8_absorb_decode_partials.restype = ctypes.c_int
+    L.kv8_absorb_decode_partials.argtypes = dec[:-1] + [i32, i32, vp, sz, vp]
+    L.kv8_lse_merge.restype = ctypes.c_int
+    L.kv8_lse_merge.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, vp]
     L.kv8_encode_bits.restype = ctypes.c_int
     L.kv8_encode_bits.argtypes = [u32, u64, vp, vp]
     L.kv8_decode_codes.restype = ctypes.c_int
@@ -137,12 +146,15 @@ def _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out):
     pln = _check(kv_len, "kv_len", torch.int32, 1)
     if kv_start.numel() != B or kv_len.numel() != B:
         raise ValueError("kv_start and kv_len need one entry per sequence")
+    args = [pql, pqr, pc, ps, pst, pln, int(max_len), B, Q, H, KV_LORA, ROPE]
+    if out is False:  # the call has no output tensor
+        return args, None, None
     if out is None:
         out = torch.empty((B, Q, H, KV_LORA), dtype=torch.float32, device=q_lat.device)
     po = _check(out, "out", torch.float32, 4)
     if tuple(out.shape) != (B, Q, H, KV_LORA):
         raise ValueError("out must be [B,Q,H,512]")
-    return [pql, pqr, pc, ps, pst, pln, int(max_len), B, Q, H, KV_LORA, ROPE], out, po
+    return args, out, po
 
 
 def absorb_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, softmax_scale,
@@ -170,6 +182,40 @@ def absorb_decode_splitT(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len
     pw = _check(workspace, "workspace", torch.uint8, 1)
     _call("kv8_absorb_decode_splitT", *args, ctypes.c_float(softmax_scale), po,
           int(num_splits), pw, workspace.numel(), _stream(stream))
+    return out
+
+
+def decode_plan(B, Q, H, max_len):
+    """(split_tokens, num_splits) that absorb_decode uses for these shapes."""
+    a, n = ctypes.c_int32(), ctypes.c_int32()
+    _call("kv8_decode_plan", B, Q, H, int(max_len), ctypes.byref(a), ctypes.byref(n))
+    return a.value, n.value
+
+
+def partials_bytes(B, Q, H, num_splits):
+    return int(lib().kv8_partials_bytes(B, Q, H, KV_LORA, num_splits))
+
+
+def absorb_decode_partials(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len,
+                           softmax_scale, split_tokens, num_splits, partials, stream=None):
+    """Stage 1 of the decode: one partial softmax per token range into
+    `partials` (f32 GPU tensor of partials_bytes() bytes)."""
+    torch = _torch()
+    args, _, _ = _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, False)
+    pp = _check(partials, "partials", torch.float32, 1)
+    _call("kv8_absorb_decode_partials", *args, ctypes.c_float(softmax_scale),
+          int(split_tokens), int(num_splits), pp, partials.numel() * 4, _stream(stream))
+
+
+def lse_merge(partials, B, Q, H, num_splits, softmax_scale, out=None, stream=None):
+    """Stage 2 of the decode: log-sum-exp merge of the partials into out."""
+    torch = _torch()
+    pp = _check(partials, "partials", torch.float32, 1)
+    if out is None:
+        out = torch.empty((B, Q, H, KV_LORA), dtype=torch.float32, device=partials.device)
+    po = _check(out, "out", torch.float32, 4)
+    _call("kv8_lse_merge", pp, B, Q, H, KV_LORA, int(num_splits), ctypes.c_float(softmax_scale),
+          po, _stream(stream))
     return out
 
 

@@ -135,6 +135,67 @@ size_t kv8_splitT_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lo
     return total > 1 ? kv8::splitT_workspace_bytes(B, Q, H, total) : 0;
 }
 
+int kv8_decode_plan(int32_t B, int32_t Q, int32_t H, int32_t max_len, int32_t* split_tokens,
+                    int32_t* num_splits) {
+    if (B < 1 || Q < 1 || H < 1 || max_len < 0 || !split_tokens || !num_splits) return KV8_EINVAL;
+    // token ranges of a fixed size (a multiple of the 32-token tile) so that
+    // B x row blocks x ranges fills the compute units
+    const int64_t units = static_cast<int64_t>(B) * row_blocks(Q, H);
+    int64_t splits = (kTargetBlocks + units - 1) / units;
+    const int64_t by_len = (static_cast<int64_t>(max_len) + 1023) / 1024;
+    splits = splits < by_len ? splits : by_len;
+    if (splits <= 1) {
+        *split_tokens = max_len;
+        *num_splits = 1;
+        return KV8_OK;
+    }
+    int64_t chunk = (max_len + splits - 1) / splits;
+    chunk = (chunk + 31) / 32 * 32;
+    *split_tokens = static_cast<int32_t>(chunk);
+    *num_splits = static_cast<int32_t>((max_len + chunk - 1) / chunk);
+    return KV8_OK;
+}
+
+size_t kv8_partials_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t num_splits) {
+    if (B < 1 || Q < 1 || H < 1 || num_splits < 1 || kv_lora != kv8::kKvLora) return 0;
+    return kv8::splitT_workspace_bytes(B, Q, H, num_splits);
+}
+
+int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
+                               const uint8_t* codes, const float* scales,
+                               const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
+                               int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                               float softmax_scale, int32_t split_tokens, int32_t num_splits,
+                               float* partials, size_t partials_bytes, void* stream) {
+    int rc = check_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, B, Q, H,
+                          kv_lora, rope, softmax_scale, partials /* no out */);
+    if (rc != KV8_OK) return rc;
+    if (num_splits < 1 || num_splits > (1 << 20) || split_tokens < 0) return KV8_EINVAL;
+    if (!partials || !aligned(partials, 256) ||
+        partials_bytes < kv8::splitT_workspace_bytes(B, Q, H, num_splits))
+        return KV8_EWORKSPACE;
+    kv8::DecodeLaunch d = make_launch(q_lat, q_rope, codes, scales, kv_start, kv_len, B, Q, H,
+                                      softmax_scale, nullptr);
+    d.n_splits = num_splits;
+    d.split_chunk = split_tokens;
+    d.n_sub = 1;
+    d.workspace = partials;
+    return launched(kv8::launch_absorb_decode(d, static_cast<hipStream_t>(stream), false));
+}
+
+int kv8_lse_merge(const float* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                  int32_t num_splits, float softmax_scale, float* out, void* stream) {
+    if (B < 1 || Q < 1 || H < 1 || num_splits < 1) return KV8_EINVAL;
+    if (kv_lora != kv8::kKvLora) return KV8_EUNSUPPORTED;
+    if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16)) return KV8_EINVAL;
+    if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
+        softmax_scale == -INFINITY)
+        return KV8_EINVAL;
+    const float sc = softmax_scale == 0.0f ? 1.17549435e-38f : softmax_scale;
+    return launched(kv8::launch_lse_merge(partials, B, Q * H, num_splits, sc, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,
                       const float* scales, const int64_t* kv_start, const int32_t* kv_len,
                       int32_t max_len, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
@@ -145,18 +206,11 @@ int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8
     hipStream_t st = static_cast<hipStream_t>(stream);
     kv8::DecodeLaunch d =
         make_launch(q_lat, q_rope, codes, scales, kv_start, kv_len, B, Q, H, softmax_scale, out);
-    // token ranges of a fixed size (a multiple of the 32-token tile) so that
-    // B x row blocks x ranges fills the compute units
-    const int64_t units = static_cast<int64_t>(B) * row_blocks(Q, H);
-    int64_t splits = (kTargetBlocks + units - 1) / units;
-    const int64_t by_len = (static_cast<int64_t>(max_len) + 1023) / 1024;
-    splits = splits < by_len ? splits : by_len;
+    int32_t chunk = 0, splits = 1;
+    kv8_decode_plan(B, Q, H, max_len, &chunk, &splits);
     if (splits <= 1) return launched(kv8::launch_absorb_decode(d, st));
-    int64_t chunk = (max_len + splits - 1) / splits;
-    chunk = (chunk + 31) / 32 * 32;
-    splits = (max_len + chunk - 1) / chunk;
-    d.n_splits = static_cast<int>(splits);
-    d.split_chunk = static_cast<int>(chunk);
+    d.n_splits = splits;
+    d.split_chunk = chunk;
     const size_t bytes = kv8::splitT_workspace_bytes(B, Q, H, d.n_splits);
     if (hipMallocAsync(&d.workspace, bytes, st) != hipSuccess) return KV8_ENOMEM;
     rc = launched(kv8::launch_absorb_decode(d, st));

@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                    "+a"(O[6]), "+a"(O[7]), "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]),
                    "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
     const float l_tot = pair_sum(l_run);
-    if (p.n_splits == 1) {
+    if (p.part_o == nullptr) {
         // the probabilities carried 2^-e: out = 2^e O / l
         if (g == 0) s_row[w][l32] = l_tot > 0.0f ? __builtin_ldexpf(1.0f / l_tot, e) : 0.0f;
     } else {
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         if (g == 0) s_row[w][l32] = __builtin_ldexpf(1.0f, e);  // partial O in true units
     }
     __builtin_amdgcn_wave_barrier();
-    float* dst = p.n_splits == 1
+    float* dst = p.part_o == nullptr
                      ? p.out + static_cast<int64_t>(b) * p.QH * kKvLora
                      : p.part_o + (static_cast<int64_t>(split) * p.B + b) * p.QH * kKvLora;
 #pragma unroll
@@ -530,7 +530,7 @@ size_t splitT_workspace_bytes(int B, int Q, int H, int n_splits) {
     return rows * kKvLora * sizeof(float) + rows * 2 * sizeof(float);
 }
 
-int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream) {
+int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) {
     DecodeArgs a;
     a.q_lat = d.q_lat;
     a.q_rope = d.q_rope;
@@ -550,7 +550,7 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream) {
     a.out = d.out;
     a.part_o = nullptr;
     a.part_ml = nullptr;
-    if (d.n_splits > 1) {
+    if (d.n_splits > 1 || !merge) {
         const size_t rows = static_cast<size_t>(d.n_splits) * d.B * a.QH;
         a.part_o = static_cast<float*>(d.workspace);
         a.part_ml = a.part_o + rows * kKvLora;
@@ -559,12 +559,21 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream) {
     hipLaunchKernelGGL(absorb_decode_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
                        0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;
-    if (d.n_splits > 1) {
+    if (d.n_splits > 1 && merge) {
         hipLaunchKernelGGL(lse_merge_kernel, dim3(static_cast<uint32_t>(d.B * a.QH)), dim3(128), 0,
                            stream, a.part_o, a.part_ml, d.B, a.QH, d.n_splits, a.c, d.out);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;
+}
+
+int launch_lse_merge(const float* partials, int B, int QH, int n_splits, float softmax_scale,
+                     float* out, hipStream_t stream) {
+    const size_t rows = static_cast<size_t>(n_splits) * B * QH;
+    const float* ml = partials + rows * kKvLora;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3(static_cast<uint32_t>(B * QH)), dim3(128), 0, stream,
+                       partials, ml, B, QH, n_splits, softmax_scale * 1.4426950408889634f, out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace kv8

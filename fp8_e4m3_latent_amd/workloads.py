@@ -50,6 +50,18 @@ def _queries(rng_lat, rng_rope, B, Q, H, kv_lora=KV_LORA, rope=ROPE):
     return bf16_bits(q_lat), bf16_bits(q_rope)
 
 
+def queries(seed, B, Q, H):
+    """bf16 (q_lat, q_rope) of shape [B,Q,H,512] / [B,Q,H,64], std 1/24."""
+    r_ql, r_qr = _streams(seed, 2)
+    return _queries(r_ql, r_qr, B, Q, H)
+
+
+def fresh_rows(seed, n):
+    """n new f32 latent rows ~N(0,1) (the rows a decode step appends)."""
+    (r,) = _streams(seed, 1)
+    return r.standard_normal((n, D), dtype=np.float32)
+
+
 @dataclass
 class DecodeWorkload:
     """Inputs of one absorbed decode over a quantized latent cache."""

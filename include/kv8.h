@@ -122,8 +122,11 @@ size_t kv8_splitT_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lo
  * kernels for long slots).  Same arguments and result as kv8_absorb_decode;
  * the rows [0, kv_len[b]) of every sequence are cut into num_splits equal
  * ranges of ceil(kv_len[b] / num_splits) rows (the last ones may be short or
- * empty), each range yields a partial softmax (running max, sum, weighted
- * context), and the partials are merged by log-sum-exp.  workspace is a
+ * empty), each range yields a partial softmax (reference maximum, sum,
+ * weighted context), and the partials are merged by log-sum-exp.  When
+ * B * ceil(Q*H/128) * num_splits is below the number of compute units, each
+ * range is further cut into equal sub-ranges so that every compute unit has
+ * one; their partials enter the same merge.  workspace is a
  * caller-owned device buffer of at least
  * kv8_splitT_workspace_bytes(B, Q, H, kv_lora, num_splits) bytes, 256-byte
  * aligned; its contents on entry do not matter. */
@@ -134,6 +137,42 @@ int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope,
                              float softmax_scale, float* out,
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* ---- Two-stage form of the decode (used by kv8_absorb_decode itself) ----
+ * Stage 1 writes one partial softmax per (token range, sequence, query row);
+ * stage 2 merges the partials by log-sum-exp.  Partials of several devices
+ * holding different token ranges of one sequence can be merged the same way.
+ *
+ * Partials buffer (device, f32, caller-owned, 256-byte aligned), R = Q*H:
+ *   O  [num_splits][B][R][kv_lora]  sum_t 2^(c (x_t - m)) scale_Lc[t] dec(Lc_t)
+ *   ml [num_splits][B][R][2]        m = reference score, l = sum_t 2^(c (x_t - m))
+ * with x_t = q_lat . xhat_Lc[t] + q_rope . xhat_Rc[t] (before softmax_scale),
+ * c = softmax_scale * log2(e); a range with no visible row has l = 0. */
+
+/* Bytes of a partials buffer for these shapes. */
+size_t kv8_partials_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t num_splits);
+
+/* The split kv8_absorb_decode chooses for these shapes: *num_splits ranges of
+ * *split_tokens rows each (num_splits == 1: no split, direct output). */
+int kv8_decode_plan(int32_t B, int32_t Q, int32_t H, int32_t max_len,
+                    int32_t* split_tokens, int32_t* num_splits);
+
+/* Stage 1.  Range s of sequence b is rows [s*k, (s+1)*k) of the sequence with
+ * k = split_tokens, or k = ceil(kv_len[b] / num_splits) when split_tokens is
+ * 0.  Other arguments as kv8_absorb_decode. */
+int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
+                               const uint8_t* codes, const float* scales,
+                               const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
+                               int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                               float softmax_scale, int32_t split_tokens, int32_t num_splits,
+                               float* partials, size_t partials_bytes, void* stream);
+
+/* Stage 2 ([colibri#299] PR description, follow-up: split-T kernels):
+ * out[b][r] = sum_s w_s O_s / sum_s w_s l_s over ranges with l_s > 0,
+ * w_s = 2^(c (m_s - m*)), m* the reference with the largest c m_s; zero when
+ * no range saw a row. */
+int kv8_lse_merge(const float* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                  int32_t num_splits, float softmax_scale, float* out, void* stream);
 
 /* Human-readable name of a kv8_status value (static string, never NULL). */
 const char* kv8_status_string(int status);

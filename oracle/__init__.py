@@ -59,8 +59,18 @@ def lib():
     return L
 
 
+def default_threads():
+    """Worker threads for the oracle: the CPUs this process may use, at most 16
+    (the host share that goes with one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def _p(a, t):
     return a.ctypes.data_as(t)
+
+
+def _t(threads):
+    return threads if threads and threads > 0 else default_threads()
 
 
 def decode(codes):
@@ -74,7 +84,7 @@ def encode(x, threads=0):
     """Saturating RNE e4m3 code of every f32 value in ``x``."""
     a = np.ascontiguousarray(x, dtype=np.float32)
     out = np.empty(a.shape, dtype=np.uint8)
-    lib().orc_encode_array(_p(a, _f32p), a.size, _p(out, _u8p), threads)
+    lib().orc_encode_array(_p(a, _f32p), a.size, _p(out, _u8p), _t(threads))
     return out
 
 
@@ -82,7 +92,7 @@ def encode_bits_range(first, count, threads=0, out=None):
     """Codes of the f32 values with bit patterns first .. first+count-1."""
     if out is None:
         out = np.empty(count, dtype=np.uint8)
-    lib().orc_encode_bits_range(first, count, _p(out, _u8p), threads)
+    lib().orc_encode_bits_range(first, count, _p(out, _u8p), _t(threads))
     return out
 
 
@@ -113,7 +123,7 @@ def quantize_rows(src, kv_lora=512, rope=64, dst_rows=None, n_cache_rows=None,
         dst_rows = np.ascontiguousarray(dst_rows, dtype=np.int64)
         dp = _p(dst_rows, _i64p)
     lib().orc_quantize_rows(_p(a, _f32p), a.strides[0] // 4, n, kv_lora, rope,
-                            _p(codes, _u8p), _p(scales, _f32p), dp, threads)
+                            _p(codes, _u8p), _p(scales, _f32p), dp, _t(threads))
     return codes, scales
 
 
@@ -147,7 +157,7 @@ def attention(q_lat, q_rope, codes, scales, kv_start, kv_len, Q=1,
                              _p(scales, _f32p), _p(kv_start, _i64p), _p(kv_len, _i32p),
                              B, Q, H, kv_lora, rope, float(softmax_scale), num_splits,
                              None if sel is None else _p(sel, _i64p),
-                             0 if sel is None else sel.size, _p(out, _f64p), threads)
+                             0 if sel is None else sel.size, _p(out, _f64p), _t(threads))
     if rc != 0:
         raise ValueError("orc_attention: bad arguments")
     return out
@@ -166,7 +176,7 @@ def attention_f32rows(q_lat, q_rope, rows, kv_start, kv_len, Q=1,
                                      _p(kv_len, _i32p), B, Q, H, kv_lora, rope,
                                      float(softmax_scale), num_splits,
                                      None if sel is None else _p(sel, _i64p),
-                                     0 if sel is None else sel.size, _p(out, _f64p), threads)
+                                     0 if sel is None else sel.size, _p(out, _f64p), _t(threads))
     if rc != 0:
         raise ValueError("orc_attention_f32rows: bad arguments")
     return out

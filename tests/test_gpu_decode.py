@@ -209,3 +209,49 @@ def test_ragged_full_size_sampled(kv8):
     """B=64, lengths U[1k, 64k], Q=4 causal, whole cache quantized on the GPU."""
     w = workloads.ragged(seed=0)
     run_case(kv8, w, sel=sample_rows(w.B, w.Q, w.H, 48, 13))
+
+
+def test_two_stage_equals_single_call(kv8):
+    """kv8_absorb_decode_partials + kv8_lse_merge with kv8_decode_plan's split
+    reproduces kv8_absorb_decode bit for bit."""
+    w = workloads.tiny(seed=21, B=4, Q=1, H=128, T=4000, outlier_p=0.0)
+    codes, scales, c, s = build_cache(kv8, w.rows)
+    ql, qr, st, ln = to_dev(w)
+    a = kv8.absorb_decode(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale)
+    k, n = kv8.decode_plan(w.B, w.Q, w.H, w.max_len)
+    assert n > 1
+    part = torch.empty(kv8.partials_bytes(w.B, w.Q, w.H, n) // 4, dtype=torch.float32,
+                       device="cuda")
+    kv8.absorb_decode_partials(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale, k, n,
+                               part)
+    b = kv8.lse_merge(part, w.B, w.Q, w.H, n, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_partials_of_two_shards_merge(kv8):
+    """Token ranges computed separately (as two devices holding halves of each
+    sequence would) merge into the full decode."""
+    w = workloads.tiny(seed=22, B=2, Q=1, H=32, T=3000, outlier_p=0.0)
+    codes, scales, c, s = build_cache(kv8, w.rows)
+    ql, qr, st, ln = to_dev(w)
+    half = w.kv_len // 2
+    shards = [(st, torch.from_numpy(half.astype(np.int32)).cuda()),
+              (st + torch.from_numpy(half.astype(np.int64)).cuda(),
+               torch.from_numpy((w.kv_len - half).astype(np.int32)).cuda())]
+    R = w.Q * w.H
+    parts = []
+    for s0, l0 in shards:
+        p = torch.empty(kv8.partials_bytes(w.B, w.Q, w.H, 1) // 4, dtype=torch.float32,
+                        device="cuda")
+        kv8.absorb_decode_partials(ql, qr, codes, scales, s0, l0, w.max_len, w.softmax_scale,
+                                   0, 1, p)
+        parts.append(p)
+    n_o = w.B * R * KL
+    merged = torch.cat([parts[0][:n_o], parts[1][:n_o], parts[0][n_o:], parts[1][n_o:]])
+    out = kv8.lse_merge(merged, w.B, w.Q, w.H, 2, w.softmax_scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention(w.q_lat, w.q_rope, c, s, w.kv_start, w.kv_len, Q=w.Q,
+                           softmax_scale=w.softmax_scale)
+    e = rel_err(out.cpu().numpy().reshape(-1, KL), ref.reshape(-1, KL))
+    assert e <= TOL, e

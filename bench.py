@@ -238,6 +238,20 @@ def _decode_workload_leg(torch, kv8, w, steps, splits=None):
                             "gb_per_s": qbytes / (qt * 1e-3) / 1e9}}
 
 
+def leg_copy(torch, steps):
+    """Plain 1 GiB device copy: the reference for scaling HBM byte counters."""
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    ms = timer_call(torch, steps, lambda: y.copy_(x))
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "ms": ms,
+            "gb_per_s": 8.0 * n / (ms * 1e-3) / 1e9}
+
+
 def timer_call(torch, steps, fn):
     timer = Timer(torch, 2, steps)
     for t in range(steps):
@@ -260,7 +274,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="decode,quantize,splitT",
-                    help="comma list of decode, quantize, splitT, ragged")
+                    help="comma list of decode, quantize, splitT, ragged, copy")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048,
                     help="query rows the oracle times for the CPU baseline (0: skip)")
     args = ap.parse_args()
@@ -294,6 +308,8 @@ def main():
         log("splitT: 256k-token slot, 64 ranges")
         extra["splitT_256k"] = _decode_workload_leg(torch, kv8, W.long_context(seed=0),
                                                     max(5, args.steps // 2), splits=64)
+    if "copy" in legs:
+        extra["copy_1gib"] = leg_copy(torch, 3)
     if "ragged" in legs:
         log("ragged: B=64, lengths U[1k,64k], Q=4")
         extra["ragged_q4"] = _decode_workload_leg(torch, kv8, W.ragged(seed=0),

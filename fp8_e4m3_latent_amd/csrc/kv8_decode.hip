@@ -11,14 +11,19 @@
 // range.  Wave w owns rows 32w..32w+31 for the whole computation:
 //
 //   tiles of 32 tokens are copied global -> LDS by the direct-to-LDS loads
-//   (3 buffers, two tiles in flight), as raw fp8 rows whose 16-byte chunks
-//   are rotated by token/4 so the score-pass reads spread over the banks;
+//   (three raw fp8 buffers, two tiles in flight); while the MFMAs work on
+//   tile i, all 256 threads decode tile i+1 once, exactly, into an fp16
+//   staging tile (rows padded to 1168 bytes so that the operand reads below
+//   hit distinct banks);
 //
 //   score pass  S^T[token, row] = dec(KV)[token, 0:576] . q[row, 0:576]
-//               36 MFMA 32x32x16 bf16 per tile, A = exactly decoded fp8 rows,
-//               B = the wave's 32 query rows (resident in VGPRs), separate
-//               accumulators for the Lc (512) and Rc (64) columns so the two
-//               row scales are applied after the dot product;
+//               36 MFMA 32x32x16 f16 per tile, A = staged fp16 rows
+//               (ds_read_b128), B = the wave's 32 query rows resident in VGPRs
+//               as fp16 (each row scaled by a power of two so its largest
+//               element sits in [2^14, 2^15): every bf16 input is then exact
+//               in fp16 unless it is 2^32 times smaller than the row maximum);
+//               separate accumulators for the Lc (512) and Rc (64) columns so
+//               the two row scales are applied after the dot product;
 //
 //   softmax     per row, with weights 2^(c (x - m)), c = softmax_scale log2(e);
 //               a lane holds one row and 16 of the tile's tokens, so row maxima
@@ -34,40 +39,47 @@
 //   context     O[row, 0:512] += (p * s_Lc / 2^e)[row, token] . dec(Lc)[token, :]
 //               32 MFMA 32x32x16 f16 per tile; the probabilities come straight
 //               from the score accumulator registers (their token order is the
-//               MFMA K order), the Lc operand is read with the LDS transpose
-//               load ds_read_b64_tr_b8, and 2^e normalises the largest Lc scale
+//               MFMA K order), the staged Lc operand is read with the LDS
+//               transpose load ds_read_b64_tr_b16, and 2^e normalises the largest Lc scale
 //               of the block's token range below 1 so p * s / 2^e fits fp16.
 //               fp16 rather than bf16 carries the probabilities: one bf16
 //               rounding of p already costs ~1e-3 of the output, fp16 ~1e-4,
 //               at the same MFMA rate, and every e4m3 value is exact in fp16.
 //
+// Both passes therefore run on fp16 MFMA: every e4m3 value and every
+// (row-scaled) bf16 query element is exact in fp16, so the score products are
+// the exact products of the dequantized cache and the queries.
+//
 // A block either writes the normalised output (one token range per
-// sequence) or a partial (O, running max M, sum l) that the log-sum-exp merge
-// kernel combines.
+// sequence) or a partial (O, reference score m, sum l) that the log-sum-exp
+// merge kernel combines.
+#include <cfloat>
 #include "kv8_device.hpp"
 #include "kv8_internal.hpp"
 
 namespace kv8 {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kTT = 32;                          // tokens per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 32 * kWaves;       // 128 query rows
-constexpr int kNBuf = 3;                         // LDS tile buffers
-constexpr int kChunks = kRowBytes / 16;          // 36 chunks of 16 B per token row
-constexpr int kTileBytes = kTT * kRowBytes;      // 18432
-constexpr int kDmaPerTile = kTileBytes / 1024;   // 18 wave-wide 1 KiB copies
+constexpr int kNRaw = 3;                         // raw fp8 tile buffers
+constexpr int kNDec = 2;                         // decoded fp16 tile buffers
+constexpr int kChunks = kRowBytes / 16;          // 36 score k-steps of 16 columns
+constexpr int kRawBytes = kTT * kRowBytes;       // 18432
+constexpr int kDecStride = 2 * kRowBytes + 16;   // 1168: fp16 token row + padding
+constexpr int kDecBytes = kTT * kDecStride;      // 37376
+constexpr int kDmaPerTile = kRawBytes / 1024;    // 18 wave-wide 1 KiB copies
 constexpr int kDmaSlots = (kDmaPerTile + kWaves - 1) / kWaves;  // 5 per wave at most
+constexpr int kDecChunks = kRawBytes / 8 / kThreads;            // 9 x 8 codes per thread
+constexpr int kScoreAhead = 4;                   // score operand loads in flight
 constexpr float kLazyLog2 = 15.0f;
-constexpr int kQReg = 30;                        // score k-steps whose q lives in VGPRs
-constexpr int kQLds = kChunks - kQReg;           // the rest is read from LDS per tile
 
 struct DecodeArgs {
     const uint16_t* q_lat;
@@ -82,24 +94,45 @@ struct DecodeArgs {
     int split_chunk;   // > 0: fixed tokens per range
     int n_sub;         // split_chunk == 0: sub-ranges per equal range
     float c;           // softmax_scale * log2(e)
-    float* out;        // [B][QH][512] when n_splits == 1
-    float* part_o;     // [n_splits][B][QH][512] when n_splits > 1
-    float* part_ml;    // [n_splits][B][QH][2]: reference score m (before c), sum l
+    float* out;        // [B][QH][512] when no partials are written
+    float* part_o;     // [n_splits][B][QH][512]
+    float* part_ml;    // [n_splits][B][QH][2]: reference score m, sum l
 };
 
-__device__ __forceinline__ void wait_vmcnt_4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
-__device__ __forceinline__ void wait_vmcnt_0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-__device__ __forceinline__ bf16x8_t dec8_bf16(uint32_t w0, uint32_t w1) {
-    uint4 u = make_uint4(dec2_bf16<false>(w0), dec2_bf16<true>(w0), dec2_bf16<false>(w1),
-                         dec2_bf16<true>(w1));
-    return __builtin_bit_cast(bf16x8_t, u);
+// s_waitcnt with only the vector-memory counter limited (lgkm and exp free)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-__device__ __forceinline__ f16x8_t dec8_f16(uint32_t w0, uint32_t w1) {
-    uint4 u = make_uint4(dec2_f16<false>(w0), dec2_f16<true>(w0), dec2_f16<false>(w1),
-                         dec2_f16<true>(w1));
-    return __builtin_bit_cast(f16x8_t, u);
+// Direct global -> LDS copies, written as inline assembly.  The compiler then
+// does not see them write LDS and inserts no wait for them before LDS reads
+// (for a copy it knows of it would wait until every copy in flight has
+// landed, serialising the tile pipeline); the kernel instead waits for each
+// tile's copies itself with s_waitcnt vmcnt, which counts these copies.  M0
+// holds the LDS byte address; the bytes of lane l land at M0 + size * l.  M0
+// is written one wait state before the copy reads it.
+__device__ __forceinline__ void copy_to_lds_b128(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void copy_to_lds_b32(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)p));
+}
+
+// 8 e4m3 codes (two dwords) -> 8 fp16 values, exact
+__device__ __forceinline__ uint4 dec8_f16(uint32_t w0, uint32_t w1) {
+    return make_uint4(dec2_f16<false>(w0), dec2_f16<true>(w0), dec2_f16<false>(w1),
+                      dec2_f16<true>(w1));
 }
 
 // Combine a per-lane value with the one in lane l ^ 32 (the other half of the
@@ -116,57 +149,19 @@ __device__ __forceinline__ float pair_sum(float v) { return v + other_half(v); }
 // write of an operand needs before an MFMA reads it (the compiler cannot see
 // that the asm is an MFMA); back-to-back MFMAs on the same accumulator need
 // none.
-__device__ __forceinline__ void mfma_score(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                 : "+v"(acc)
-                 : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma_score(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-// Context MFMA with the accumulator pinned to AGPRs (same hazard note as
-// above).
+// Context MFMA with the accumulator pinned to AGPRs (same hazard note).
 __device__ __forceinline__ void mfma_ctx(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Wait states between the last score MFMA and the first VALU read of its
-// accumulator (conservatively more than the 16-pass result latency).
+// accumulator (conservatively more than the result latency).
 __device__ __forceinline__ void mfma_score_drain(f32x16_t& a0, f32x16_t& a1) {
     asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    h2 r = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// LDS address of byte `col` (multiple of 8) of token row t in a tile: chunk
-// c = col/16 sits at chunk slot (c + t/4) mod 36 of row t.
-__device__ __forceinline__ int tile_addr(int t, int col) {
-    int slot = (col >> 4) + (t >> 2);
-    slot = slot >= kChunks ? slot - kChunks : slot;
-    return t * kRowBytes + 16 * slot + (col & 15);
-}
-
-// O[dt] += P (32 rows x 16 tokens, two k-steps) . dec(Lc) (16 tokens x 32 dims)
-// for the 16 dim tiles of 32 latent columns.
-__device__ __forceinline__ void context_pass(f32x16_t (&O)[16], const uint4 (&pa)[2],
-                                             const uint8_t* kvb, const int (&ctx_base)[2],
-                                             const int (&ctx_slot)[2]) {
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-        const f16x8_t A = __builtin_bit_cast(f16x8_t, pa[kc]);
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) {
-            int off = ctx_base[kc] + 32 * dt;
-            if (dt >= 14) off = ctx_slot[kc] + 2 * dt >= kChunks ? off - kRowBytes : off;
-            const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2_t*)(kvb + off));
-            const f16x8_t bv =
-                dec8_f16(static_cast<uint32_t>(raw[0]), static_cast<uint32_t>(raw[1]));
-            mfma_ctx(O[dt], A, bv);
-        }
-    }
 }
 
 // Zero a context accumulator in place (an MFMA of zeros with a zero C operand),
@@ -176,17 +171,76 @@ __device__ __forceinline__ void zero_acc(f32x16_t& acc) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "+a"(acc) : "v"(z));
 }
 
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 r = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// bf16 bits -> f32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) {
+    return max((w << 16) & 0x7FFFFFFFu, w & 0x7FFF0000u);
+}
+
+// 8 bf16 values times 2^-k -> 8 fp16 values (exact for the scaled range)
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 q, int k) {
+    uint4 r;
+    r.x = pack_f16x2(__builtin_ldexpf(bf16_lo(q.x), -k), __builtin_ldexpf(bf16_hi(q.x), -k));
+    r.y = pack_f16x2(__builtin_ldexpf(bf16_lo(q.y), -k), __builtin_ldexpf(bf16_hi(q.y), -k));
+    r.z = pack_f16x2(__builtin_ldexpf(bf16_lo(q.z), -k), __builtin_ldexpf(bf16_hi(q.z), -k));
+    r.w = pack_f16x2(__builtin_ldexpf(bf16_lo(q.w), -k), __builtin_ldexpf(bf16_hi(q.w), -k));
+    return r;
+}
+
+// Lc operand of context MFMA n = 16 kc + dt: two transpose loads of the fp16
+// staging tile, 4 tokens each (tokens 8 apart: second half of the k-group)
+__device__ __forceinline__ f16x8_t ctx_operand(const uint8_t* dec_lane, int n) {
+    const int off = (n >> 4) * 16 * kDecStride + 64 * (n & 15);
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(dec_lane + off));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(dec_lane + off + 8 * kDecStride));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo);
+    const uint2 h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(f16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
+// O[dt] += P (32 rows x 16 tokens, two k-steps) . dec(Lc) (16 tokens x 32 dims)
+// for the 16 dim tiles of 32 latent columns; the operand loads run kCtxAhead
+// MFMAs ahead.
+constexpr int kCtxAhead = 3;
+__device__ __forceinline__ void context_pass(f32x16_t (&O)[16], const uint4 (&pa)[2],
+                                             const uint8_t* dec_lane) {
+    f16x8_t bq[kCtxAhead];
+#pragma unroll
+    for (int n = 0; n < kCtxAhead; ++n) bq[n] = ctx_operand(dec_lane, n);
+#pragma unroll
+    for (int n = 0; n < 32; ++n) {
+        // (the scheduler may not sink the loads next to their MFMAs: the asm
+        //  MFMAs carry no latency it could see)
+        __builtin_amdgcn_sched_barrier(0);
+        const f16x8_t bv = bq[n % kCtxAhead];
+        if (n + kCtxAhead < 32) bq[n % kCtxAhead] = ctx_operand(dec_lane, n + kCtxAhead);
+        mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pa[n >> 4]), bv);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t s_kv[kNBuf][kTileBytes];
-    __shared__ __attribute__((aligned(16))) float s_sc[kNBuf][2 * kTT];
-    __shared__ __attribute__((aligned(16))) uint4 s_q[kWaves][kQLds > 0 ? kQLds : 1][64];
-    __shared__ int s_restart;
+    __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kNRaw][kRawBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_dec[kNDec][kDecBytes];
+    __shared__ __attribute__((aligned(16))) float s_sc[kNRaw][2 * kTT];
+    __shared__ __attribute__((aligned(16))) float s_scd[kNDec][2 * kTT];
     __shared__ __attribute__((aligned(16))) float s_row[kWaves][32];
     __shared__ uint32_t s_red[kWaves];
+    __shared__ int s_restart;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;        // lane half
     const int l32 = lane & 31;
 
@@ -229,20 +283,31 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int64_t n_row = row_ok ? L - (p.Q - 1) + row / p.H : 0;
     const int64_t lim_row = n_row < te ? n_row : te;
 
-    // ---- query rows of this wave: B operand of the score MFMA (row l32,
-    //      columns 16ks + 8g .. +8): k-steps below kQReg stay in VGPRs, the
-    //      others in this wave's LDS slice.  Rows past Q*H (block padding)
-    //      reuse row 0; their results are never stored.
-    uint4 qv[kQReg];
+    // ---- query row l32 of this wave: B operand of the score MFMA (columns
+    //      16ks + 8g .. +8), fp16 after scaling the row by 2^-kq so that its
+    //      largest magnitude lies in [2^12, 2^13): every bf16 element above
+    //      2^-27 of the row maximum converts exactly.  Rows past
+    //      Q*H (block padding) reuse row 0; their results are never stored.
+    uint4 qv[kChunks];
+    int kq = 0;
     {
         const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
         const uint4* ql = reinterpret_cast<const uint4*>(p.q_lat + qrow * kKvLora);
         const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
 #pragma unroll
-        for (int ks = 0; ks < kQReg; ++ks) qv[ks] = ql[2 * ks + g];
+        for (int ks = 0; ks < kChunks; ++ks) qv[ks] = ks < 32 ? ql[2 * ks + g] : qr[2 * (ks - 32) + g];
+        uint32_t mbits = 0;
 #pragma unroll
-        for (int ks = kQReg; ks < kChunks; ++ks)
-            s_q[w][ks - kQReg][lane] = ks < 32 ? ql[2 * ks + g] : qr[2 * (ks - 32) + g];
+        for (int ks = 0; ks < kChunks; ++ks)
+            mbits = max(max(mbits, max(absmax_bf16x2(qv[ks].x), absmax_bf16x2(qv[ks].y))),
+                        max(absmax_bf16x2(qv[ks].z), absmax_bf16x2(qv[ks].w)));
+        const float qmax = pair_max(__uint_as_float(mbits));
+        if (qmax > 0.0f) {
+            kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 12;
+            kq = kq < -100 ? -100 : (kq > 120 ? 120 : kq);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kChunks; ++ks) qv[ks] = bf16x8_to_f16(qv[ks], kq);
     }
 
     // ---- 2^e above the largest Lc scale of the token range
@@ -259,22 +324,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         e = e < -126 ? -126 : e;
     }
 
-    // ---- direct-to-LDS copy plan: wave w issues copies i = w + 4k; lane's
-    //      16-byte chunk is tile slot 64 i + lane = token tt, rotated slot cs
-    int dma_src[kDmaSlots];  // (tt << 16) | byte offset of the chunk in the token row
-#pragma unroll
-    for (int k = 0; k < kDmaSlots; ++k) {
-        const int i = w + kWaves * k;
-        const int slot = 64 * i + lane;
-        const int tt = slot / kChunks;
-        const int cs = slot - tt * kChunks;
-        int c = cs - (tt >> 2);
-        c = c < 0 ? c + kChunks : c;
-        dma_src[k] = (tt << 16) | (16 * c);
-    }
-
+    // ---- tile copies: wave w issues the 1 KiB copies i = w + 4k of a tile
+    //      (lane's 16 bytes = tile byte 1024 i + 16 lane, token (64 i + lane)/36)
     auto issue_tile = [&](int tile) {
-        const int buf = tile % kNBuf;
+        const int buf = tile % kNRaw;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const int valid = static_cast<int>(te - t0 < kTT ? te - t0 : kTT);
         const uint8_t* src = p.codes + (row_base + t0) * kRowBytes;
@@ -282,56 +335,74 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         for (int k = 0; k < kDmaSlots; ++k) {
             const int i = w + kWaves * k;
             if (i < kDmaPerTile) {
-                int tt = dma_src[k] >> 16;
-                tt = tt < valid ? tt : valid - 1;
-                const uint8_t* gp = src + tt * kRowBytes + (dma_src[k] & 0xFFFF);
-                __builtin_amdgcn_global_load_lds(gp, (lds_u8*)&s_kv[buf][1024 * i], 16, 0, 0);
+                const int slot = 64 * i + lane;
+                int tt = slot / kChunks;
+                const int cc = slot - tt * kChunks;
+                tt = tt < valid ? tt : valid - 1;  // past the range: repeat its last row
+                copy_to_lds_b128(src + tt * kRowBytes + 16 * cc, lds_addr(&s_raw[buf][1024 * i]));
             }
         }
         if (w == kWaves - 1) {  // the tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane
             int tt = lane >> 1;
             tt = tt < valid ? tt : valid - 1;
-            const float* gp = p.scales + 2 * (row_base + t0 + tt) + (lane & 1);
-            __builtin_amdgcn_global_load_lds(gp, (lds_u8*)&s_sc[buf][0], 4, 0, 0);
+            copy_to_lds_b32(p.scales + 2 * (row_base + t0 + tt) + (lane & 1), lds_addr(&s_sc[buf][0]));
         }
     };
+    // wait until the copies of an issued tile have landed, `later` tiles
+    // having been issued after it (each wave issues at least 4 copies a tile)
+    auto wait_tile = [&](int later) {
+        if (later >= 2) wait_vmcnt<8>();
+        else if (later == 1) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+    };
 
-    // ---- per-lane LDS offsets
+    // ---- decode stage: the 8 threads of token tid/8 convert its codes
+    //      8 (tid % 8) + 64 j, j < 9, into the fp16 staging tile
+    const int raw_off = (tid >> 3) * kRowBytes + 8 * (tid & 7);
+    const int dec_off = (tid >> 3) * kDecStride + 16 * (tid & 7);
+    auto decode_tile = [&](int tile) {
+        const uint8_t* raw = &s_raw[tile % kNRaw][raw_off];
+        uint8_t* dst = &s_dec[tile % kNDec][dec_off];
+        uint2 r[kDecChunks];
+#pragma unroll
+        for (int j = 0; j < kDecChunks; ++j) r[j] = *reinterpret_cast<const uint2*>(raw + 64 * j);
+#pragma unroll
+        for (int j = 0; j < kDecChunks; ++j)
+            *reinterpret_cast<uint4*>(dst + 128 * j) = dec8_f16(r[j].x, r[j].y);
+        if (tid < 2 * kTT) s_scd[tile % kNDec][tid] = s_sc[tile % kNRaw][tid];
+    };
+
+    // ---- per-lane LDS offsets in a staging tile
     // score A operand: token l32, columns 16ks + 8g
-    const int sc_base = tile_addr(l32, 8 * g);
-    // context B operand (transpose load): in the 16-lane group G = lane/16,
-    // lane i supplies token tau(g, i/2) + 16 kc and column 16 (2dt + G%2) + 8 (i%2)
+    const int sc_off = l32 * kDecStride + 16 * g;
+    // context B operand: in the 16-lane group G = lane/16 (k-group g = G/2,
+    // dims 32dt + 16(G%2) + 0..15), transpose load h of k-step kc takes token
+    // tau(g, 4h + gi/4) + 16kc at dims +4(gi%4), tau(g, s) = 4g + s + 4[s >= 4]
     const int G = lane >> 4;
     const int gi = lane & 15;
-    const int kk = gi >> 1;
-    const int tau = 4 * g + kk + (kk >= 4 ? 4 : 0);
-    int ctx_base[2], ctx_slot[2];  // offset of dim tile 0 and its rotated chunk slot
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-        const int tok = 16 * kc + tau;
-        ctx_slot[kc] = (G & 1) + (tok >> 2);  // <= 8, no wrap for dim tile 0
-        ctx_base[kc] = tok * kRowBytes + 16 * ctx_slot[kc] + 8 * (gi & 1);
-    }
+    const int ctx_off = (4 * g + (gi >> 2)) * kDecStride + 32 * (G & 1) + 8 * (gi & 3);
 
     f32x16_t O[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) O[dt][j] = 0.0f;
-    // Scores x are kept before the factor c = softmax_scale * log2(e); the
-    // row's reference m_x is its largest x (smallest when c < 0), and the
-    // weights are p = 2^(c (x - m_x)): the difference is taken first, so the
+    // Scores x are kept in accumulator units (before the factor
+    // c_row = softmax_scale * log2(e) * 2^kq); the row's reference m_x is its
+    // largest x (smallest when c < 0), and the weights are
+    // p = 2^(c_row (x - m_x)): the difference is taken first, so the
     // reference token gets exactly 1 at any score magnitude.
-    const float c = p.c;
-    const float mask_val = c >= 0.0f ? -INFINITY : INFINITY;  // masked x, and "no reference"
+    // (clamped to the finite normal range so that c_row (x - m_x) is 0 at the
+    // reference and -inf at masked tokens, never NaN)
+    float c_row = __builtin_ldexpf(p.c, kq);
+    if (!(fabsf(c_row) <= FLT_MAX)) c_row = copysignf(FLT_MAX, p.c);
+    if (fabsf(c_row) < FLT_MIN) c_row = copysignf(FLT_MIN, p.c);
+    const float mask_val = c_row >= 0.0f ? -INFINITY : INFINITY;  // masked x, "no reference"
     float m_x = mask_val;
     float l_run = 0.0f;        // this lane's half of the row sum
-    // token offsets (relative to the range start) this lane's row may see
-    const int64_t lim_rel0 = lim_row - ts;
+    const int64_t lim_rel0 = lim_row - ts;  // visible tokens of this row from the range start
 
     if (tid == 0) s_restart = 0;
-    if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
 
     // At most two passes over the token range: a row whose later tile exceeds
     // its reference maximum by more than kLazyLog2 raises the reference and
@@ -339,33 +410,46 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // kLazyLog2 of every tile maximum) and the range is then run once more
     // from a zero accumulator.
     for (int attempt = 0; attempt < 2; ++attempt) {
-        for (int it = 0; it < ntiles; ++it) {
-            if (it + 1 < ntiles) wait_vmcnt_4(); else wait_vmcnt_0();
+        // prologue: three tiles in flight, the first one decoded
+        if (ntiles > 0) issue_tile(0);
+        if (ntiles > 1) issue_tile(1);
+        if (ntiles > 2) issue_tile(2);
+        if (ntiles > 0) {
+            wait_tile(ntiles > 2 ? 2 : ntiles - 1);
             __syncthreads();
-            if (it + 2 < ntiles) issue_tile(it + 2);
-            const int buf = it % kNBuf;
-            const uint8_t* kvb = &s_kv[buf][0];
+            decode_tile(0);
+        }
+        for (int it = 0; it < ntiles; ++it) {
+            if (it + 1 < ntiles) wait_tile(it + 2 < ntiles ? 1 : 0);
+            __syncthreads();
+            if (it + 3 < ntiles) issue_tile(it + 3);
+            if (it + 1 < ntiles) decode_tile(it + 1);
+            const uint8_t* dec = &s_dec[it % kNDec][0];
+            const float* scd = &s_scd[it % kNDec][0];
 
             // ---------------- score pass
             f32x16_t accL, accR;
 #pragma unroll
             for (int j = 0; j < 16; ++j) { accL[j] = 0.0f; accR[j] = 0.0f; }
+            // (operand loads run kScoreAhead MFMAs ahead)
+            f16x8_t aq[kScoreAhead];
+#pragma unroll
+            for (int ks = 0; ks < kScoreAhead; ++ks)
+                aq[ks] = *reinterpret_cast<const f16x8_t*>(dec + sc_off + 32 * ks);
 #pragma unroll
             for (int ks = 0; ks < kChunks; ++ks) {
-                int off = sc_base + 16 * ks;
-                if (ks >= kChunks - 8) {  // the rotated slot may wrap to the row start
-                    const int slot = ks + (l32 >> 2);
-                    off = slot >= kChunks ? off - kRowBytes : off;
-                }
-                const uint2 raw = *reinterpret_cast<const uint2*>(kvb + off);
-                const bf16x8_t a = dec8_bf16(raw.x, raw.y);
-                const bf16x8_t qb =
-                    __builtin_bit_cast(bf16x8_t, ks < kQReg ? qv[ks] : s_q[w][ks - kQReg][lane]);
+                __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead
+                const f16x8_t a = aq[ks % kScoreAhead];
+                if (ks + kScoreAhead < kChunks)
+                    aq[ks % kScoreAhead] =
+                        *reinterpret_cast<const f16x8_t*>(dec + sc_off + 32 * (ks + kScoreAhead));
+                const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[ks]);
                 if (ks < 32)
                     mfma_score(accL, a, qb);
                 else
                     mfma_score(accR, a, qb);
             }
+            __builtin_amdgcn_sched_barrier(0);
             mfma_score_drain(accL, accR);
 
             // ---------------- scale, mask, softmax (row l32, tokens
@@ -373,10 +457,9 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             float x[16], sL[16];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 s01 =
-                    *reinterpret_cast<const float4*>(&s_sc[buf][2 * (8 * q4 + 4 * g)]);
+                const float4 s01 = *reinterpret_cast<const float4*>(&scd[2 * (8 * q4 + 4 * g)]);
                 const float4 s23 =
-                    *reinterpret_cast<const float4*>(&s_sc[buf][2 * (8 * q4 + 4 * g) + 4]);
+                    *reinterpret_cast<const float4*>(&scd[2 * (8 * q4 + 4 * g) + 4]);
                 const float lsc[4] = {s01.x, s01.z, s23.x, s23.z};
                 const float rsc[4] = {s01.y, s01.w, s23.y, s23.w};
 #pragma unroll
@@ -396,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 }
             }
             float mx = x[0];
-            if (c >= 0.0f) {
+            if (c_row >= 0.0f) {
 #pragma unroll
                 for (int j = 1; j < 16; ++j) mx = fmaxf(mx, x[j]);
                 mx = pair_max(mx);
@@ -407,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             }
             if (m_x == mask_val) {
                 m_x = mx;  // nothing accumulated for this row yet
-            } else if (c * (mx - m_x) > kLazyLog2) {
+            } else if (c_row * (mx - m_x) > kLazyLog2) {
                 m_x = mx;
                 s_restart = 1;
             }
@@ -416,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             float lsum = 0.0f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float pj = __builtin_amdgcn_exp2f(c * (x[j] - ref));
+                const float pj = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
                 lsum += pj;
                 pf[j] = pj * __builtin_ldexpf(sL[j], -e);
             }
@@ -431,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 pa[kc].z = pack_f16x2(pf[8 * kc + 4], pf[8 * kc + 5]);
                 pa[kc].w = pack_f16x2(pf[8 * kc + 6], pf[8 * kc + 7]);
             }
-            context_pass(O, pa, kvb, ctx_base, ctx_slot);
+            context_pass(O, pa, dec + ctx_off);
         }
         __syncthreads();
         if (!s_restart) break;
@@ -440,10 +523,8 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 #pragma unroll
         for (int dt = 0; dt < 16; ++dt) zero_acc(O[dt]);
         l_run = 0.0f;
-        if (ntiles > 0) issue_tile(0);
-        if (ntiles > 1) issue_tile(1);
     }
-    wait_vmcnt_0();  // no tile copy may land after the block has finished
+    wait_vmcnt<0>();  // no tile copy may land after the block has finished
 
     // ---------------- epilogue: rows of O register j are 8(j/4) + 4g + j%4
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -457,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     } else {
         if (g == 0 && row_ok) {
             float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 2;
-            ml[0] = m_x;
+            ml[0] = __builtin_ldexpf(m_x, kq);  // reference score in true units
             ml[1] = l_tot;
         }
         if (g == 0) s_row[w][l32] = __builtin_ldexpf(1.0f, e);  // partial O in true units

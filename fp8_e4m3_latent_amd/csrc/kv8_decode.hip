@@ -54,6 +54,7 @@
 // sequence) or a partial (O, reference score m, sum l) that the log-sum-exp
 // merge kernel combines.
 #include <cfloat>
+#include <utility>
 #include "kv8_device.hpp"
 #include "kv8_internal.hpp"
 
@@ -69,16 +70,15 @@ constexpr int kTT = 32;                          // tokens per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 32 * kWaves;       // 128 query rows
-constexpr int kNRaw = 3;                         // raw fp8 tile buffers
-constexpr int kNDec = 2;                         // decoded fp16 tile buffers
-constexpr int kChunks = kRowBytes / 16;          // 36 score k-steps of 16 columns
-constexpr int kRawBytes = kTT * kRowBytes;       // 18432
-constexpr int kDecStride = 2 * kRowBytes + 16;   // 1168: fp16 token row + padding
-constexpr int kDecBytes = kTT * kDecStride;      // 37376
+constexpr int kNBuf = 3;                         // raw and decoded tile buffers each
+constexpr int kRawBytes = kTT * kRowBytes;       // 18432: 32 token rows of codes
+constexpr int kRopeRegion = kTT * kKvLora;       // Rc codes start here in a raw tile
+constexpr int kLcStride = 2 * kKvLora + 64;      // 1088: fp16 Lc row + padding
+constexpr int kLcBytes = kTT * kLcStride;        // 34816
 constexpr int kDmaPerTile = kRawBytes / 1024;    // 18 wave-wide 1 KiB copies
 constexpr int kDmaSlots = (kDmaPerTile + kWaves - 1) / kWaves;  // 5 per wave at most
-constexpr int kDecChunks = kRawBytes / 8 / kThreads;            // 9 x 8 codes per thread
-constexpr int kScoreAhead = 4;                   // score operand loads in flight
+constexpr int kScoreAhead = 3;                   // score operand loads in flight
+constexpr int kCtxAhead = 3;                     // context operand loads in flight
 constexpr float kLazyLog2 = 15.0f;
 
 struct DecodeArgs {
@@ -112,17 +112,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // landed, serialising the tile pipeline); the kernel instead waits for each
 // tile's copies itself with s_waitcnt vmcnt, which counts these copies.  M0
 // holds the LDS byte address; the bytes of lane l land at M0 + size * l.  M0
-// is written one wait state before the copy reads it.
-__device__ __forceinline__ void copy_to_lds_b128(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// is written one wait state before the copy reads it.  The source address
+// is a wave-uniform base (SGPR pair) plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void copy_to_lds_b128(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(src), "s"(lds)
+                 : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void copy_to_lds_b32(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+__device__ __forceinline__ void copy_to_lds_b32(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :
-                 : "v"(src), "s"(lds)
+                 : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -140,15 +141,17 @@ __device__ __forceinline__ uint4 dec8_f16(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ float other_half(float v) {
     return __shfl_xor(v, 32, 64);
 }
-__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, other_half(v)); }
-__device__ __forceinline__ float pair_min(float v) { return fminf(v, other_half(v)); }
 __device__ __forceinline__ float pair_sum(float v) { return v + other_half(v); }
 
-// Score MFMA with its accumulator pinned to VGPRs, leaving all 256 AGPRs to the
-// context accumulator.  The leading s_nop 1 gives the two wait states a VALU
-// write of an operand needs before an MFMA reads it (the compiler cannot see
-// that the asm is an MFMA); back-to-back MFMAs on the same accumulator need
-// none.
+// Score MFMAs with their accumulator pinned to VGPRs, leaving all 256 AGPRs to
+// the context accumulator.  The leading s_nop 1 gives the two wait states a
+// VALU write of an operand needs before an MFMA reads it (the compiler cannot
+// see that the asm is an MFMA); back-to-back MFMAs on the same accumulator
+// need none.  The first MFMA of a chain starts from a zero C operand.
+__device__ __forceinline__ void mfma_score_first(f32x16_t& acc, const f16x8_t& a,
+                                                 const f16x8_t& b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ void mfma_score(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
@@ -161,7 +164,7 @@ __device__ __forceinline__ void mfma_ctx(f32x16_t& acc, const f16x8_t& a, const 
 // Wait states between the last score MFMA and the first VALU read of its
 // accumulator (conservatively more than the result latency).
 __device__ __forceinline__ void mfma_score_drain(f32x16_t& a0, f32x16_t& a1) {
-    asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
 }
 
 // Zero a context accumulator in place (an MFMA of zeros with a zero C operand),
@@ -170,6 +173,22 @@ __device__ __forceinline__ void zero_acc(f32x16_t& acc) {
     const f16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "+a"(acc) : "v"(z));
 }
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded in the source:
+// the pipelined phases select their work per step with `if constexpr`.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Instruction order inside the software-pipelined phases is fixed in the
+// source: the scheduler cannot see the latency of the asm MFMAs and would
+// otherwise pull loads down next to their uses.
+__device__ __forceinline__ void order() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -195,45 +214,39 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 q, int k) {
     return r;
 }
 
+template <typename T>
+__device__ __forceinline__ T lds_load(const uint8_t* base, int off) {
+    return *reinterpret_cast<const T*>(base + off);
+}
+
 // Lc operand of context MFMA n = 16 kc + dt: two transpose loads of the fp16
-// staging tile, 4 tokens each (tokens 8 apart: second half of the k-group)
-__device__ __forceinline__ f16x8_t ctx_operand(const uint8_t* dec_lane, int n) {
-    const int off = (n >> 4) * 16 * kDecStride + 64 * (n & 15);
+// tile, 4 tokens each (the second half of the lane's k-group is 8 tokens on)
+__device__ __forceinline__ f16x8_t ctx_operand(const uint8_t* lc, int tb0, int tb1, int n) {
+    const int off = (n >> 4) * 16 * kLcStride + 64 * (n & 15);
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4_t*)(dec_lane + off));
+        (__attribute__((address_space(3))) i16x4_t*)(lc + tb0 + off));
     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4_t*)(dec_lane + off + 8 * kDecStride));
+        (__attribute__((address_space(3))) i16x4_t*)(lc + tb1 + off));
     const uint2 l2 = __builtin_bit_cast(uint2, lo);
     const uint2 h2 = __builtin_bit_cast(uint2, hi);
     return __builtin_bit_cast(f16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
 
-// O[dt] += P (32 rows x 16 tokens, two k-steps) . dec(Lc) (16 tokens x 32 dims)
-// for the 16 dim tiles of 32 latent columns; the operand loads run kCtxAhead
-// MFMAs ahead.
-constexpr int kCtxAhead = 3;
-__device__ __forceinline__ void context_pass(f32x16_t (&O)[16], const uint4 (&pa)[2],
-                                             const uint8_t* dec_lane) {
-    f16x8_t bq[kCtxAhead];
-#pragma unroll
-    for (int n = 0; n < kCtxAhead; ++n) bq[n] = ctx_operand(dec_lane, n);
-#pragma unroll
-    for (int n = 0; n < 32; ++n) {
-        // (the scheduler may not sink the loads next to their MFMAs: the asm
-        //  MFMAs carry no latency it could see)
-        __builtin_amdgcn_sched_barrier(0);
-        const f16x8_t bv = bq[n % kCtxAhead];
-        if (n + kCtxAhead < 32) bq[n % kCtxAhead] = ctx_operand(dec_lane, n + kCtxAhead);
-        mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pa[n >> 4]), bv);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
+// LDS layouts of a tile (32 tokens t; chunks are 16 bytes):
+//   raw    Lc codes of t, chunk q (< 32), at chunk 32 t + (q ^ 8 ((t >> 2) & 1));
+//          Rc codes of t, chunk c (< 4), at chunk 1024 + 32 c + t.  The tile
+//          copies place the chunks there (each lane picks its source chunk).
+//   fp16   Lc values of t, chunk c (< 64), at byte 1088 t + 16 (c ^ ((t >> 2) & 3)).
+// With 64 LDS banks of 4 bytes every read and write below touches each bank
+// once per 256 bytes: the score operand reads (16 tokens, one chunk each),
+// the transpose reads (4 tokens x 64 bytes per 32 lanes), the decode reads
+// (tokens t and t + 4) and writes (tokens t and t + 4, both chunk parities).
 
 __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kNRaw][kRawBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_dec[kNDec][kDecBytes];
-    __shared__ __attribute__((aligned(16))) float s_sc[kNRaw][2 * kTT];
-    __shared__ __attribute__((aligned(16))) float s_scd[kNDec][2 * kTT];
+    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kNBuf][kRawBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_lc[kNBuf][kLcBytes];
+    __shared__ __attribute__((aligned(16))) float s_sc[kNBuf][2 * kTT];   // copied (Lc, Rc) scales
+    __shared__ __attribute__((aligned(16))) float s_scd[kNBuf][3 * kTT];  // s_Lc, s_Rc, s_Lc / 2^e
     __shared__ __attribute__((aligned(16))) float s_row[kWaves][32];
     __shared__ uint32_t s_red[kWaves];
     __shared__ int s_restart;
@@ -283,70 +296,52 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int64_t n_row = row_ok ? L - (p.Q - 1) + row / p.H : 0;
     const int64_t lim_row = n_row < te ? n_row : te;
 
-    // ---- query row l32 of this wave: B operand of the score MFMA (columns
-    //      16ks + 8g .. +8), fp16 after scaling the row by 2^-kq so that its
-    //      largest magnitude lies in [2^12, 2^13): every bf16 element above
-    //      2^-27 of the row maximum converts exactly.  Rows past
-    //      Q*H (block padding) reuse row 0; their results are never stored.
-    uint4 qv[kChunks];
-    int kq = 0;
+    // ---- tile copies.  Wave w issues the 1 KiB copies i = w + 4k of a tile;
+    //      the 16 bytes of lane l land at raw chunk 64 i + l, whose source
+    //      chunk (token, offset in the token's row) follows the raw layout.
+    //      Copy k < 4 (i < 16, Lc) takes token 2 w + lane / 32 + 8 k, whose
+    //      chunk swizzle does not depend on k; copy 4 (i = 16, 17) takes Rc
+    //      chunk 2 (i - 16) + lane / 32 of token lane % 32.
+    int dma_lc, dma_rc;
     {
-        const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
-        const uint4* ql = reinterpret_cast<const uint4*>(p.q_lat + qrow * kKvLora);
-        const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
-#pragma unroll
-        for (int ks = 0; ks < kChunks; ++ks) qv[ks] = ks < 32 ? ql[2 * ks + g] : qr[2 * (ks - 32) + g];
-        uint32_t mbits = 0;
-#pragma unroll
-        for (int ks = 0; ks < kChunks; ++ks)
-            mbits = max(max(mbits, max(absmax_bf16x2(qv[ks].x), absmax_bf16x2(qv[ks].y))),
-                        max(absmax_bf16x2(qv[ks].z), absmax_bf16x2(qv[ks].w)));
-        const float qmax = pair_max(__uint_as_float(mbits));
-        if (qmax > 0.0f) {
-            kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 12;
-            kq = kq < -100 ? -100 : (kq > 120 ? 120 : kq);
-        }
-#pragma unroll
-        for (int ks = 0; ks < kChunks; ++ks) qv[ks] = bf16x8_to_f16(qv[ks], kq);
+        const int t = 2 * w + (lane >> 5);
+        dma_lc = t * kRowBytes + 16 * ((lane & 31) ^ (8 * ((t >> 2) & 1)));
+        dma_rc = (lane & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (lane >> 5));
     }
-
-    // ---- 2^e above the largest Lc scale of the token range
-    uint32_t rbits = 0;
-    for (int64_t t = ts + tid; t < te; t += kThreads)
-        rbits = max(rbits, __float_as_uint(p.scales[2 * (row_base + t)]));
-    rbits = wave_max_u32(rbits);
-    if (lane == 0) s_red[w] = rbits;
-    __syncthreads();
-    rbits = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
-    int e = 0;
-    if (rbits != 0) {
-        e = static_cast<int>((rbits >> 23) & 0xFF) - 126;  // r < 2^e
-        e = e < -126 ? -126 : e;
-    }
-
-    // ---- tile copies: wave w issues the 1 KiB copies i = w + 4k of a tile
-    //      (lane's 16 bytes = tile byte 1024 i + 16 lane, token (64 i + lane)/36)
-    auto issue_tile = [&](int tile) {
-        const int buf = tile % kNRaw;
+    // copy slot k < kDmaSlots: the wave's code copy k; slot kDmaSlots: the
+    // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (last wave)
+    auto issue_copy = [&](int tile, int buf, int k) {
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const int valid = static_cast<int>(te - t0 < kTT ? te - t0 : kTT);
-        const uint8_t* src = p.codes + (row_base + t0) * kRowBytes;
-#pragma unroll
-        for (int k = 0; k < kDmaSlots; ++k) {
+        if (k < kDmaSlots) {
             const int i = w + kWaves * k;
             if (i < kDmaPerTile) {
-                const int slot = 64 * i + lane;
-                int tt = slot / kChunks;
-                const int cc = slot - tt * kChunks;
-                tt = tt < valid ? tt : valid - 1;  // past the range: repeat its last row
-                copy_to_lds_b128(src + tt * kRowBytes + 16 * cc, lds_addr(&s_raw[buf][1024 * i]));
+                // The per-lane offset is unsigned: it must never go negative.
+                // A full tile folds the first token of copy k (8 k) into the
+                // base; a partial one keeps the tile start as base and clamps
+                // the token past the range to its last row.
+                const int kt = k < 4 ? 8 * k : 0;
+                if (valid == kTT) {
+                    copy_to_lds_b128(p.codes + (row_base + t0 + kt) * kRowBytes,
+                                     k < 4 ? dma_lc : dma_rc, lds_addr(&s_raw[buf][1024 * i]));
+                } else {
+                    int off = (k < 4 ? dma_lc : dma_rc) + kt * kRowBytes;
+                    const int t = off / kRowBytes;
+                    if (t >= valid) off -= (t - (valid - 1)) * kRowBytes;
+                    copy_to_lds_b128(p.codes + (row_base + t0) * kRowBytes, off,
+                                     lds_addr(&s_raw[buf][1024 * i]));
+                }
             }
-        }
-        if (w == kWaves - 1) {  // the tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane
+        } else if (w == kWaves - 1) {
             int tt = lane >> 1;
             tt = tt < valid ? tt : valid - 1;
-            copy_to_lds_b32(p.scales + 2 * (row_base + t0 + tt) + (lane & 1), lds_addr(&s_sc[buf][0]));
+            copy_to_lds_b32(p.scales + 2 * (row_base + t0), 4 * (2 * tt + (lane & 1)),
+                            lds_addr(&s_sc[buf][0]));
         }
+    };
+    auto issue_tile = [&](int tile) {  // (tile < kNBuf)
+#pragma unroll
+        for (int k = 0; k <= kDmaSlots; ++k) issue_copy(tile, tile, k);
     };
     // wait until the copies of an issued tile have landed, `later` tiles
     // having been issued after it (each wave issues at least 4 copies a tile)
@@ -356,51 +351,259 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         else wait_vmcnt<0>();
     };
 
-    // ---- decode stage: the 8 threads of token tid/8 convert its codes
-    //      8 (tid % 8) + 64 j, j < 9, into the fp16 staging tile
-    const int raw_off = (tid >> 3) * kRowBytes + 8 * (tid & 7);
-    const int dec_off = (tid >> 3) * kDecStride + 16 * (tid & 7);
-    auto decode_tile = [&](int tile) {
-        const uint8_t* raw = &s_raw[tile % kNRaw][raw_off];
-        uint8_t* dst = &s_dec[tile % kNDec][dec_off];
-        uint2 r[kDecChunks];
-#pragma unroll
-        for (int j = 0; j < kDecChunks; ++j) r[j] = *reinterpret_cast<const uint2*>(raw + 64 * j);
-#pragma unroll
-        for (int j = 0; j < kDecChunks; ++j)
-            *reinterpret_cast<uint4*>(dst + 128 * j) = dec8_f16(r[j].x, r[j].y);
-        if (tid < 2 * kTT) s_scd[tile % kNDec][tid] = s_sc[tile % kNRaw][tid];
-    };
+    // the first three tiles are in flight while the queries load
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    if (ntiles > 2) issue_tile(2);
 
-    // ---- per-lane LDS offsets in a staging tile
-    // score A operand: token l32, columns 16ks + 8g
-    const int sc_off = l32 * kDecStride + 16 * g;
-    // context B operand: in the 16-lane group G = lane/16 (k-group g = G/2,
-    // dims 32dt + 16(G%2) + 0..15), transpose load h of k-step kc takes token
-    // tau(g, 4h + gi/4) + 16kc at dims +4(gi%4), tau(g, s) = 4g + s + 4[s >= 4]
-    const int G = lane >> 4;
-    const int gi = lane & 15;
-    const int ctx_off = (4 * g + (gi >> 2)) * kDecStride + 32 * (G & 1) + 8 * (gi & 3);
+    // ---- 2^e above the largest Lc scale of the token range
+    uint32_t rbits = 0;
+    for (int64_t t = ts + tid; t < te; t += kThreads)
+        rbits = max(rbits, __float_as_uint(p.scales[2 * (row_base + t)]));
+
+    // ---- query row l32 of this wave: B operand of the score MFMA, fp16 after
+    //      scaling the row by 2^-kq so that its largest magnitude lies in
+    //      [2^12, 2^13): every bf16 element above 2^-27 of the row maximum
+    //      converts exactly.  Lc k-step ks holds columns 16 ks + 8 g .. +8;
+    //      Rc k-step r holds rope columns 32 g + 8 r .. +8 (the Rc operand
+    //      below takes the same order).  Rows past Q*H (block padding) reuse
+    //      row 0; their results are never stored.
+    uint4 qv[36];
+    int kq = 0;
+    {
+        const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
+        const uint4* ql = reinterpret_cast<const uint4*>(p.q_lat + qrow * kKvLora);
+        const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) qv[ks] = ql[2 * ks + g];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qv[32 + r] = qr[4 * g + r];
+        uint32_t mbits = 0;
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks)
+            mbits = max(max(mbits, max(absmax_bf16x2(qv[ks].x), absmax_bf16x2(qv[ks].y))),
+                        max(absmax_bf16x2(qv[ks].z), absmax_bf16x2(qv[ks].w)));
+        const float qmax = fmaxf(__uint_as_float(mbits), other_half(__uint_as_float(mbits)));
+        if (qmax > 0.0f) {
+            kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 12;
+            kq = kq < -100 ? -100 : (kq > 120 ? 120 : kq);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) qv[ks] = bf16x8_to_f16(qv[ks], kq);
+    }
+
+    rbits = wave_max_u32(rbits);
+    if (lane == 0) s_red[w] = rbits;
+    __syncthreads();
+    rbits = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+    int e = 0;
+    if (rbits != 0) {
+        e = static_cast<int>((rbits >> 23) & 0xFF) - 126;  // r < 2^e
+        e = e < -126 ? -126 : e;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+
+    // ---- per-lane LDS offsets
+    // score A operand, Lc k-step ks: token l32, chunk 2 ks + g
+    const int hsw = (l32 >> 2) & 3;
+    const int sc_base0 = l32 * kLcStride + 16 * (g ^ hsw);        // ks even (+64 (ks >> 1))
+    const int sc_base1 = l32 * kLcStride + 16 * ((2 + g) ^ hsw);  // ks odd
+    // score A operand, Rc: token l32, chunks 2 g and 2 g + 1
+    const int rope_off = kRopeRegion + 16 * (64 * g + l32);
+    // context B operand: lane (G = lane / 16, gi = lane % 16) of k-group g
+    // takes token 4 g + 8 h + gi / 4 (+ 16 kc) at dims 32 dt + 16 (G % 2) +
+    // 4 (gi % 4) for its transpose load h
+    const int G = lane >> 4, gi = lane & 15;
+    const int cG = 2 * (G & 1) + ((gi & 3) >> 1);
+    const int tb0 = (4 * g + (gi >> 2)) * kLcStride + 16 * (cG ^ (g & 3)) + 8 * (gi & 1);
+    const int tb1 = (4 * g + 8 + (gi >> 2)) * kLcStride + 16 * (cG ^ ((g + 2) & 3)) + 8 * (gi & 1);
+    // decode: lane 16 a + 8 bb + s of wave w converts token 8 w + a + 4 bb,
+    // raw chunks 8 j + s (j < 4) into fp16 chunks 16 j + 2 s, 16 j + 2 s + 1
+    const int d_bb = (lane >> 3) & 1, d_s = lane & 7;
+    const int d_t = 8 * w + (lane >> 4) + 4 * d_bb;
+    // (raw chunk 8 j + s sits at 8 (j ^ bb) + s; fp16 chunk 2 s + 1 is
+    //  chunk 2 s with bit 4 of the byte offset flipped)
+    const int d_rA = 512 * d_t + 16 * d_s + 128 * d_bb;         // j = 0, 2 (+256); j odd: ^ 128
+    const int d_hs = (d_t >> 2) & 3;
+    const int d_wA = d_t * kLcStride + 16 * ((2 * d_s) ^ d_hs);  // + 256 j; odd chunk: ^ 16
+
+    // Scores x are kept in accumulator units times sgn = sign(c) (the row
+    // scales carry the sign), so that with c_row = |softmax_scale log2(e)| 2^kq
+    // the weights are p = 2^(c_row (x - m_x)) with m_x the row's largest x: the
+    // difference is taken first, so the reference token gets exactly 1 at any
+    // score magnitude.  (c_row is clamped to the finite normal range so that
+    // c_row (x - m_x) is 0 at the reference and -inf at masked tokens, never
+    // NaN.)
+    const float sgn = p.c >= 0.0f ? 1.0f : -1.0f;  // (uniform)
+    float c_row = __builtin_ldexpf(fabsf(p.c), kq);
+    if (!(c_row <= FLT_MAX)) c_row = FLT_MAX;
+    if (c_row < FLT_MIN) c_row = FLT_MIN;
+    const float mask_val = -INFINITY;  // masked x, and "no reference yet"
+    float m_x = mask_val;
+    float l_run = 0.0f;        // this lane's half of the row sum
+    const int lim_rel0 = static_cast<int>(lim_row - ts);  // visible tokens of the row in the range
 
     f32x16_t O[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) O[dt][j] = 0.0f;
-    // Scores x are kept in accumulator units (before the factor
-    // c_row = softmax_scale * log2(e) * 2^kq); the row's reference m_x is its
-    // largest x (smallest when c < 0), and the weights are
-    // p = 2^(c_row (x - m_x)): the difference is taken first, so the
-    // reference token gets exactly 1 at any score magnitude.
-    // (clamped to the finite normal range so that c_row (x - m_x) is 0 at the
-    // reference and -inf at masked tokens, never NaN)
-    float c_row = __builtin_ldexpf(p.c, kq);
-    if (!(fabsf(c_row) <= FLT_MAX)) c_row = copysignf(FLT_MAX, p.c);
-    if (fabsf(c_row) < FLT_MIN) c_row = copysignf(FLT_MIN, p.c);
-    const float mask_val = c_row >= 0.0f ? -INFINITY : INFINITY;  // masked x, "no reference"
-    float m_x = mask_val;
-    float l_run = 0.0f;        // this lane's half of the row sum
-    const int64_t lim_rel0 = lim_row - ts;  // visible tokens of this row from the range start
+
+    // ---- pipeline stages --------------------------------------------------
+    // decode(tile): raw codes -> fp16 Lc tile, scales -> (s_Lc, s_Rc, s_Lc/2^e)
+    uint4 draw[2];
+    auto decode_load = [&](int buf, int j) {  // raw chunk 8 j + s
+        const uint8_t* raw = &s_raw[buf][0];
+        draw[j & 1] = lds_load<uint4>(raw, ((j & 1) ? (d_rA ^ 128) : d_rA) + 256 * (j >> 1));
+    };
+    auto decode_store = [&](int buf, int j, int half) {
+        uint8_t* lc = &s_lc[buf][0];
+        const uint4 r = draw[j & 1];
+        const uint4 v = half == 0 ? dec8_f16(r.x, r.y) : dec8_f16(r.z, r.w);
+        *reinterpret_cast<uint4*>(lc + (half == 0 ? d_wA : (d_wA ^ 16)) + 256 * j) = v;
+    };
+    auto decode_scales = [&](int buf) {
+        if (tid < kTT) {
+            const float sl = s_sc[buf][2 * tid];
+            const float sr = s_sc[buf][2 * tid + 1];
+            float* d = &s_scd[buf][0];
+            d[tid] = sgn * sl;
+            d[kTT + tid] = sgn * sr;
+            d[2 * kTT + tid] = __builtin_ldexpf(sl, -e);
+        }
+    };
+
+    // x(tile) = s_Lc accL + s_Rc accR for row l32 and tokens 8 (j / 4) + 4 g +
+    // j % 4 of the tile (the accumulator order), masked past the row's limit
+    float x[16];
+    f32x16_t accL, accR;
+    auto form_x = [&](int buf, int q4) {
+        const float* scd = &s_scd[buf][0];
+        const float4 sl = *reinterpret_cast<const float4*>(scd + 8 * q4 + 4 * g);
+        const float4 sr = *reinterpret_cast<const float4*>(scd + kTT + 8 * q4 + 4 * g);
+        x[4 * q4 + 0] = __builtin_fmaf(sl.x, accL[4 * q4 + 0], sr.x * accR[4 * q4 + 0]);
+        x[4 * q4 + 1] = __builtin_fmaf(sl.y, accL[4 * q4 + 1], sr.y * accR[4 * q4 + 1]);
+        x[4 * q4 + 2] = __builtin_fmaf(sl.z, accL[4 * q4 + 2], sr.z * accR[4 * q4 + 2]);
+        x[4 * q4 + 3] = __builtin_fmaf(sl.w, accL[4 * q4 + 3], sr.w * accR[4 * q4 + 3]);
+    };
+    auto mask_x = [&](int tile) {
+        if (ts + static_cast<int64_t>(tile) * kTT + kTT > full_until) {  // (uniform)
+            const int rel = lim_rel0 - tile * kTT - 4 * g;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int t = 8 * (j >> 2) + (j & 3);
+                x[j] = t < rel ? x[j] : mask_val;
+            }
+        }
+    };
+
+    // score(tile): accL = dec(Lc) . q_lat, accR = dec(Rc) . q_rope (36 MFMAs);
+    // one MFMA per step, so that other work can sit between the steps
+    f16x8_t aq[kScoreAhead];
+    uint4 rope[2];
+    f16x8_t ropeop;
+    auto score_begin = [&](int buf) {
+        const uint8_t* lc = &s_lc[buf][0];
+#pragma unroll
+        for (int k = 0; k < kScoreAhead; ++k)
+            aq[k] = lds_load<f16x8_t>(lc, (k & 1 ? sc_base1 : sc_base0) + 64 * (k >> 1));
+    };
+    auto score_step = [&](int buf, int ks) {
+        const uint8_t* lc = &s_lc[buf][0];
+        if (ks < 32) {
+            const f16x8_t a = aq[ks % kScoreAhead];
+            const int kn = ks + kScoreAhead;
+            if (kn < 32) aq[ks % kScoreAhead] = lds_load<f16x8_t>(lc, (kn & 1 ? sc_base1 : sc_base0) + 64 * (kn >> 1));
+            if (ks == 20) {  // the Rc codes of the lane's token, two chunks
+                const uint8_t* raw = &s_raw[buf][0];
+                rope[0] = lds_load<uint4>(raw, rope_off);
+                rope[1] = lds_load<uint4>(raw, rope_off + 16 * 32);
+            }
+            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[ks]);
+            if (ks == 0) mfma_score_first(accL, a, qb);
+            else mfma_score(accL, a, qb);
+            if (ks >= 31) {  // Rc operand of the next step
+                const int r = ks - 31;
+                const uint4 c4 = rope[r >> 1];
+                ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
+            }
+        } else {
+            const int r = ks - 32;
+            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[ks]);
+            if (r == 0) mfma_score_first(accR, ropeop, qb);
+            else mfma_score(accR, ropeop, qb);
+            if (r < 3) {
+                const uint4 c4 = rope[(r + 1) >> 1];
+                ropeop = __builtin_bit_cast(f16x8_t, ((r + 1) & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
+            }
+        }
+    };
+
+    // softmax(tile) on x: reference update (phase B, after x), then the
+    // weights p = 2^(c_row (x - ref)), their sum, and fp16 P' = p s_Lc / 2^e
+    // packed as the A operand of the two context k-steps (phase A)
+    uint4 pa[2];
+    float mx_part = 0.0f, mx_other = 0.0f, ref = 0.0f, lsum = 0.0f;
+    auto soft_max_local = [&]() {
+        const float m0 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        const float m1 = fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]));
+        const float m2 = fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11]));
+        const float m3 = fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]));
+        mx_part = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+    };
+    auto soft_exchange = [&]() { mx_other = other_half(mx_part); };
+    auto soft_ref = [&](bool real) {
+        const float mx = fmaxf(mx_part, mx_other);
+        const bool first = m_x == mask_val;  // nothing accumulated for this row yet
+        const bool raise = !first && c_row * (mx - m_x) > kLazyLog2;
+        m_x = real && (first || raise) ? mx : m_x;
+        if (real && raise) s_restart = 1;
+        ref = m_x == mask_val ? 0.0f : m_x;
+    };
+    float4 sev;
+    auto soft_scale_load = [&](int buf, int q4) {
+        sev = *reinterpret_cast<const float4*>(&s_scd[buf][2 * kTT + 8 * q4 + 4 * g]);
+    };
+    auto soft_weight = [&](int j) {  // x[j] <- P'[j]
+        const float pj = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
+        lsum += pj;
+        const float se = (j & 3) == 0 ? sev.x : (j & 3) == 1 ? sev.y : (j & 3) == 2 ? sev.z : sev.w;
+        x[j] = pj * se;
+    };
+    auto soft_pack = [&](int kc, int h) {
+        if (h == 0) {
+            pa[kc].x = pack_f16x2(x[8 * kc + 0], x[8 * kc + 1]);
+            pa[kc].y = pack_f16x2(x[8 * kc + 2], x[8 * kc + 3]);
+        } else {
+            pa[kc].z = pack_f16x2(x[8 * kc + 4], x[8 * kc + 5]);
+            pa[kc].w = pack_f16x2(x[8 * kc + 6], x[8 * kc + 7]);
+        }
+    };
+    auto soft_weights_all = [&](int tile) {
+        lsum = 0.0f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            soft_scale_load(tile, q4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) soft_weight(4 * q4 + r);
+        }
+        soft_pack(0, 0); soft_pack(0, 1); soft_pack(1, 0); soft_pack(1, 1);
+    };
+
+    // context(tile): O[dt] += P (32 rows x 16 tokens) . dec(Lc) (16 tokens x
+    // 32 dims), 32 MFMAs, operand loads kCtxAhead MFMAs ahead
+    f16x8_t bq[kCtxAhead];
+    auto context_begin = [&](int buf) {
+        const uint8_t* lc = &s_lc[buf][0];
+#pragma unroll
+        for (int n = 0; n < kCtxAhead; ++n) bq[n] = ctx_operand(lc, tb0, tb1, n);
+    };
+    auto context_step = [&](int buf, int n, uint4 pk) {
+        const uint8_t* lc = &s_lc[buf][0];
+        const f16x8_t bv = bq[n % kCtxAhead];
+        if (n + kCtxAhead < 32) bq[n % kCtxAhead] = ctx_operand(lc, tb0, tb1, n + kCtxAhead);
+        mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bv);
+    };
 
     if (tid == 0) s_restart = 0;
 
@@ -409,114 +612,102 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // flags the block; the pass still finishes (so every reference ends within
     // kLazyLog2 of every tile maximum) and the range is then run once more
     // from a zero accumulator.
+    //
+    // Software pipeline (tile i): copy(i) is issued three tiles ahead,
+    // decode(i) two tiles ahead; iteration i runs
+    //   phase A: score(i + 1), with the copies of tile i + 3 between its
+    //            MFMAs, then the softmax of tile i + 1 (scores, reference,
+    //            weights, packed P')
+    //   phase B: context(i), with decode(i + 2) between its MFMAs
+    // Stages past the last tile run on stale buffers and their results are
+    // never used.
     for (int attempt = 0; attempt < 2; ++attempt) {
-        // prologue: three tiles in flight, the first one decoded
-        if (ntiles > 0) issue_tile(0);
-        if (ntiles > 1) issue_tile(1);
-        if (ntiles > 2) issue_tile(2);
+        if (attempt > 0) {
+            if (ntiles > 0) issue_tile(0);
+            if (ntiles > 1) issue_tile(1);
+            if (ntiles > 2) issue_tile(2);
+        }
         if (ntiles > 0) {
-            wait_tile(ntiles > 2 ? 2 : ntiles - 1);
+            wait_tile(ntiles > 2 ? 1 : 0);  // tiles 0 and 1
             __syncthreads();
-            decode_tile(0);
-        }
-        for (int it = 0; it < ntiles; ++it) {
-            if (it + 1 < ntiles) wait_tile(it + 2 < ntiles ? 1 : 0);
-            __syncthreads();
-            if (it + 3 < ntiles) issue_tile(it + 3);
-            if (it + 1 < ntiles) decode_tile(it + 1);
-            const uint8_t* dec = &s_dec[it % kNDec][0];
-            const float* scd = &s_scd[it % kNDec][0];
-
-            // ---------------- score pass
-            f32x16_t accL, accR;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) { accL[j] = 0.0f; accR[j] = 0.0f; }
-            // (operand loads run kScoreAhead MFMAs ahead)
-            f16x8_t aq[kScoreAhead];
+            for (int tile = 0; tile < 2; ++tile) {
 #pragma unroll
-            for (int ks = 0; ks < kScoreAhead; ++ks)
-                aq[ks] = *reinterpret_cast<const f16x8_t*>(dec + sc_off + 32 * ks);
-#pragma unroll
-            for (int ks = 0; ks < kChunks; ++ks) {
-                __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead
-                const f16x8_t a = aq[ks % kScoreAhead];
-                if (ks + kScoreAhead < kChunks)
-                    aq[ks % kScoreAhead] =
-                        *reinterpret_cast<const f16x8_t*>(dec + sc_off + 32 * (ks + kScoreAhead));
-                const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[ks]);
-                if (ks < 32)
-                    mfma_score(accL, a, qb);
-                else
-                    mfma_score(accR, a, qb);
+                for (int j = 0; j < 4; ++j) {
+                    decode_load(tile, j);
+                    decode_store(tile, j, 0);
+                    decode_store(tile, j, 1);
+                }
+                decode_scales(tile);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            score_begin(0);
+            static_for<36>([&](auto ks) { score_step(0, ks); });
             mfma_score_drain(accL, accR);
-
-            // ---------------- scale, mask, softmax (row l32, tokens
-            //                  8(j/4) + 4g + j%4 of the tile)
-            float x[16], sL[16];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 s01 = *reinterpret_cast<const float4*>(&scd[2 * (8 * q4 + 4 * g)]);
-                const float4 s23 =
-                    *reinterpret_cast<const float4*>(&scd[2 * (8 * q4 + 4 * g) + 4]);
-                const float lsc[4] = {s01.x, s01.z, s23.x, s23.z};
-                const float rsc[4] = {s01.y, s01.w, s23.y, s23.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 4 * q4 + r;
-                    sL[j] = lsc[r];
-                    x[j] = __builtin_fmaf(lsc[r], accL[j], rsc[r] * accR[j]);
-                }
-            }
-            if (ts + static_cast<int64_t>(it) * kTT + kTT > full_until) {
-                const int64_t rel = lim_rel0 - static_cast<int64_t>(it) * kTT;
-                const int lim = rel < 0 ? 0 : (rel > kTT ? kTT : static_cast<int>(rel));
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int t = 8 * (j >> 2) + 4 * g + (j & 3);
-                    x[j] = t < lim ? x[j] : mask_val;
-                }
-            }
-            float mx = x[0];
-            if (c_row >= 0.0f) {
-#pragma unroll
-                for (int j = 1; j < 16; ++j) mx = fmaxf(mx, x[j]);
-                mx = pair_max(mx);
-            } else {
-#pragma unroll
-                for (int j = 1; j < 16; ++j) mx = fminf(mx, x[j]);
-                mx = pair_min(mx);
-            }
-            if (m_x == mask_val) {
-                m_x = mx;  // nothing accumulated for this row yet
-            } else if (c_row * (mx - m_x) > kLazyLog2) {
-                m_x = mx;
-                s_restart = 1;
-            }
-            const float ref = m_x == mask_val ? 0.0f : m_x;
-            float pf[16];
-            float lsum = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float pj = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
-                lsum += pj;
-                pf[j] = pj * __builtin_ldexpf(sL[j], -e);
-            }
+            for (int q4 = 0; q4 < 4; ++q4) form_x(0, q4);
+            mask_x(0);
+            soft_max_local();
+            soft_exchange();
+            soft_ref(true);
+            soft_weights_all(0);
             l_run += lsum;
-
-            // ---------------- context pass
-            uint4 pa[2];
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                pa[kc].x = pack_f16x2(pf[8 * kc + 0], pf[8 * kc + 1]);
-                pa[kc].y = pack_f16x2(pf[8 * kc + 2], pf[8 * kc + 3]);
-                pa[kc].z = pack_f16x2(pf[8 * kc + 4], pf[8 * kc + 5]);
-                pa[kc].w = pack_f16x2(pf[8 * kc + 6], pf[8 * kc + 7]);
-            }
-            context_pass(O, pa, dec + ctx_off);
         }
-        __syncthreads();
+        // iteration `it` with R = it % kNBuf known at compile time, so that
+        // every LDS address is a lane offset plus an immediate
+        auto iteration = [&](int it, auto rc) {
+            constexpr int R = decltype(rc)::value;
+            constexpr int B0 = R, B1 = (R + 1) % kNBuf, B2 = (R + 2) % kNBuf;
+            const bool real_next = it + 1 < ntiles;
+            // ---------------- phase A: score(it + 1), copies of tile it + 3,
+            //                  weights of tile it
+            const bool copy = it + 3 < ntiles;
+            score_begin(B1);
+            lsum = 0.0f;
+            order();
+            const uint4 pa0 = pa[0], pa1 = pa[1];  // P' of tile it
+            static_for<36>([&](auto kc) {
+                constexpr int ks = decltype(kc)::value;
+                score_step(B1, ks);
+                if constexpr (ks % 6 == 0) {  // one copy every 6 MFMAs
+                    if (copy) issue_copy(it + 3, B0, ks / 6);
+                }
+                order();
+            });
+            mfma_score_drain(accL, accR);
+            // softmax of tile it + 1 (its result is only used when it is real)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) form_x(B1, q4);
+            mask_x(it + 1);
+            soft_max_local();
+            soft_exchange();
+            soft_ref(real_next);
+            soft_weights_all(B1);
+            l_run += real_next ? lsum : 0.0f;
+            if (it + 2 < ntiles) wait_tile(copy ? 1 : 0);
+            __syncthreads();
+            // ---------------- phase B: context(it), decode(it + 2), the
+            //                  reference of tile it + 1
+            context_begin(B0);
+            order();
+            static_for<32>([&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                context_step(B0, n, n < 16 ? pa0 : pa1);
+                if constexpr (n == 0) decode_load(B2, 0);
+                if constexpr (n == 1) decode_load(B2, 1);
+                if constexpr (n >= 3 && n < 11) decode_store(B2, (n - 3) >> 1, (n - 3) & 1);
+                if constexpr (n == 4) decode_load(B2, 2);
+                if constexpr (n == 6) decode_load(B2, 3);
+                if constexpr (n == 12) decode_scales(B2);
+                order();
+            });
+            __syncthreads();
+        };
+        for (int it0 = 0; it0 < ntiles; it0 += kNBuf) {
+            iteration(it0, std::integral_constant<int, 0>{});
+            if (it0 + 1 < ntiles) iteration(it0 + 1, std::integral_constant<int, 1>{});
+            if (it0 + 2 < ntiles) iteration(it0 + 2, std::integral_constant<int, 2>{});
+        }
         if (!s_restart) break;
         __syncthreads();
         if (tid == 0) s_restart = 0;
@@ -538,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     } else {
         if (g == 0 && row_ok) {
             float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 2;
-            ml[0] = __builtin_ldexpf(m_x, kq);  // reference score in true units
+            ml[0] = __builtin_ldexpf(sgn * m_x, kq);  // reference score in true units
             ml[1] = l_tot;
         }
         if (g == 0) s_row[w][l32] = __builtin_ldexpf(1.0f, e);  // partial O in true units
@@ -566,32 +757,78 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 // out[b, row, :] = sum_s w_s O_s / sum_s w_s l_s over the splits with
 // l_s > 0, w_s = 2^(c (m_s - m*)) with m* the reference of largest c m_s;
 // zero when no split saw a token.
-__global__ __launch_bounds__(128) void lse_merge_kernel(const float* __restrict__ part_o,
-                                                        const float* __restrict__ part_ml,
-                                                        int B, int QH, int n_splits, float c,
-                                                        float* __restrict__ out) {
-    const int64_t br = blockIdx.x;  // b * QH + row
+//
+// Block = 256 threads = one (b, row) and one quarter (128 columns) of the
+// output row: 8 groups of 32 lanes, group g summing the splits s = g mod 8
+// (lane = 4 columns), then one reduction over the groups in LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = 8;
+constexpr int kMergeCols = kKvLora / 4;
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml,
+                                                                  int B, int QH, int n_splits, float c,
+                                                                  float* __restrict__ out) {
+    __shared__ float s_red[kMergeThreads / 64];
+    __shared__ float4 s_acc[kMergeGroups][32];
+    __shared__ float s_l[kMergeGroups];
+    const int tid = threadIdx.x;
+    const int64_t br = blockIdx.x >> 2;  // b * QH + row
+    const int col0 = (blockIdx.x & 3) * kMergeCols;
     const int64_t stride = static_cast<int64_t>(B) * QH;
-    bool any = false;
-    float mstar = 0.0f;
-    for (int s = 0; s < n_splits; ++s) {
-        const float* ml = part_ml + (s * stride + br) * 2;
-        if (ml[1] > 0.0f && (!any || c * (ml[0] - mstar) > 0.0f)) {
-            mstar = ml[0];
-            any = true;
-        }
+    const bool cpos = c >= 0.0f;
+
+    // m*: the largest (c > 0) or smallest (c < 0) reference with l > 0
+    float mm = cpos ? -INFINITY : INFINITY;
+    for (int s = tid; s < n_splits; s += kMergeThreads) {
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + (s * stride + br) * 2);
+        if (ml.y > 0.0f) mm = cpos ? fmaxf(mm, ml.x) : fminf(mm, ml.x);
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float o = __shfl_xor(mm, off, 64);
+        mm = cpos ? fmaxf(mm, o) : fminf(mm, o);
+    }
+    if ((tid & 63) == 0) s_red[tid >> 6] = mm;
+    __syncthreads();
+    mm = s_red[0];
+#pragma unroll
+    for (int k = 1; k < kMergeThreads / 64; ++k) mm = cpos ? fmaxf(mm, s_red[k]) : fminf(mm, s_red[k]);
+    const bool any = cpos ? mm > -INFINITY : mm < INFINITY;
+
+    const int grp = tid >> 5, q = tid & 31;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float lsum = 0.0f;
     if (any) {
-        for (int s = 0; s < n_splits; ++s) {
-            const float* ml = part_ml + (s * stride + br) * 2;
-            const float ls = ml[1];
-            if (ls > 0.0f) {
-                const float wgt = __builtin_amdgcn_exp2f(c * (ml[0] - mstar));
-                lsum += wgt * ls;
-                const float4 o = reinterpret_cast<const float4*>(
-                    part_o + (s * stride + br) * kKvLora)[threadIdx.x];
+        const float* po = part_o + br * kKvLora + col0 + 4 * q;
+        int s = grp;
+        // four splits in flight per lane
+        for (; s + 3 * kMergeGroups < n_splits; s += 4 * kMergeGroups) {
+            float2 ml[4];
+            float4 o[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t su = s + u * kMergeGroups;
+                ml[u] = *reinterpret_cast<const float2*>(part_ml + (su * stride + br) * 2);
+                o[u] = *reinterpret_cast<const float4*>(po + su * stride * kKvLora);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (ml[u].y > 0.0f) {
+                    const float wgt = __builtin_amdgcn_exp2f(c * (ml[u].x - mm));
+                    lsum += wgt * ml[u].y;
+                    acc.x += wgt * o[u].x;
+                    acc.y += wgt * o[u].y;
+                    acc.z += wgt * o[u].z;
+                    acc.w += wgt * o[u].w;
+                }
+            }
+        }
+        for (; s < n_splits; s += kMergeGroups) {
+            const float2 ml = *reinterpret_cast<const float2*>(part_ml + (static_cast<int64_t>(s) * stride + br) * 2);
+            if (ml.y > 0.0f) {
+                const float4 o = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s) * stride * kKvLora);
+                const float wgt = __builtin_amdgcn_exp2f(c * (ml.x - mm));
+                lsum += wgt * ml.y;
                 acc.x += wgt * o.x;
                 acc.y += wgt * o.y;
                 acc.z += wgt * o.z;
@@ -599,9 +836,75 @@ __global__ __launch_bounds__(128) void lse_merge_kernel(const float* __restrict_
             }
         }
     }
+    s_acc[grp][q] = acc;
+    if (q == 0) s_l[grp] = lsum;
+    __syncthreads();
+    if (grp == 0) {
+        float l = 0.0f;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int g2 = 0; g2 < kMergeGroups; ++g2) {
+            l += s_l[g2];
+            const float4 v = s_acc[g2][q];
+            a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        }
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        *reinterpret_cast<float4*>(out + br * kKvLora + col0 + 4 * q) =
+            make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    }
+}
+
+// The same merge for at most 64 splits: one wave per (b, row), lane s < n
+// holding split s's (m, l), every lane summing 8 columns over the splits.
+constexpr int kMergeRowsPerBlock = 4;
+__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int B, int QH,
+    int n_splits, float c, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t br = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + (threadIdx.x >> 6);
+    const int64_t stride = static_cast<int64_t>(B) * QH;
+    if (br >= stride) return;
+    const bool cpos = c >= 0.0f;
+    float2 ml = make_float2(0.0f, 0.0f);
+    if (lane < n_splits) ml = *reinterpret_cast<const float2*>(part_ml + (lane * stride + br) * 2);
+    float mm = ml.y > 0.0f ? ml.x : (cpos ? -INFINITY : INFINITY);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float o = __shfl_xor(mm, off, 64);
+        mm = cpos ? fmaxf(mm, o) : fminf(mm, o);
+    }
+    const float wgt = ml.y > 0.0f ? __builtin_amdgcn_exp2f(c * (ml.x - mm)) : 0.0f;
+    float lsum = wgt * ml.y;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+    float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+    const float* po = part_o + br * kKvLora + 4 * lane;
+    for (int s2 = 0; s2 < n_splits; ++s2) {
+        const float w2 = __shfl(wgt, s2, 64);
+        if (w2 > 0.0f) {  // (uniform)
+            const float4 o0 = *reinterpret_cast<const float4*>(po + s2 * stride * kKvLora);
+            const float4 o1 = *reinterpret_cast<const float4*>(po + s2 * stride * kKvLora + 256);
+            a0.x += w2 * o0.x; a0.y += w2 * o0.y; a0.z += w2 * o0.z; a0.w += w2 * o0.w;
+            a1.x += w2 * o1.x; a1.y += w2 * o1.y; a1.z += w2 * o1.z; a1.w += w2 * o1.w;
+        }
+    }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    reinterpret_cast<float4*>(out + br * kKvLora)[threadIdx.x] =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    float* o = out + br * kKvLora + 4 * lane;
+    *reinterpret_cast<float4*>(o) = make_float4(a0.x * inv, a0.y * inv, a0.z * inv, a0.w * inv);
+    *reinterpret_cast<float4*>(o + 256) = make_float4(a1.x * inv, a1.y * inv, a1.z * inv, a1.w * inv);
+}
+
+void launch_merge(const float* part_o, const float* part_ml, int B, int QH, int n_splits, float c,
+                  float* out, hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(B) * QH;
+    if (n_splits <= 64) {
+        hipLaunchKernelGGL(lse_merge_rows_kernel,
+                           dim3(static_cast<uint32_t>((rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
+                           dim3(64 * kMergeRowsPerBlock), 0, stream, part_o, part_ml, B, QH, n_splits, c, out);
+    } else {
+        hipLaunchKernelGGL(lse_merge_kernel, dim3(static_cast<uint32_t>(4 * rows)), dim3(kMergeThreads),
+                           0, stream, part_o, part_ml, B, QH, n_splits, c, out);
+    }
 }
 
 }  // namespace
@@ -641,8 +944,7 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) 
                        0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;
     if (d.n_splits > 1 && merge) {
-        hipLaunchKernelGGL(lse_merge_kernel, dim3(static_cast<uint32_t>(d.B * a.QH)), dim3(128), 0,
-                           stream, a.part_o, a.part_ml, d.B, a.QH, d.n_splits, a.c, d.out);
+        launch_merge(a.part_o, a.part_ml, d.B, a.QH, d.n_splits, a.c, d.out, stream);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;
@@ -652,8 +954,7 @@ int launch_lse_merge(const float* partials, int B, int QH, int n_splits, float s
                      float* out, hipStream_t stream) {
     const size_t rows = static_cast<size_t>(n_splits) * B * QH;
     const float* ml = partials + rows * kKvLora;
-    hipLaunchKernelGGL(lse_merge_kernel, dim3(static_cast<uint32_t>(B * QH)), dim3(128), 0, stream,
-                       partials, ml, B, QH, n_splits, softmax_scale * 1.4426950408889634f, out);
+    launch_merge(partials, ml, B, QH, n_splits, softmax_scale * 1.4426950408889634f, out, stream);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -50,6 +50,20 @@ __device__ __forceinline__ uint32_t encode_e4m3(float q) {
     return (a > 0x7F800000u) ? 0u : code;
 }
 
+// Four codes (one 32-bit word, value k in byte k) with the gfx950 fp8
+// conversion, which rounds to nearest even into OCP e4m3: NaN is replaced
+// by +0 first (so NaN -> 0x00) and every value is clamped to [-448, 448]
+// (so |q| >= 448 and +-inf saturate to 0x7E | sign).  Gives the same codes
+// as encode_e4m3 for every f32 input.
+__device__ __forceinline__ float sat_e4m3(float q) {
+    q = q == q ? q : 0.0f;
+    return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
+}
+__device__ __forceinline__ uint32_t encode4_e4m3_hw(float q0, float q1, float q2, float q3) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(q0), sat_e4m3(q1), 0, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(q2), sat_e4m3(q3), lo, true));
+}
+
 // |x| bit pattern if x is finite, else 0: a max over these (as unsigned
 // integers) is the largest finite magnitude.
 __device__ __forceinline__ uint32_t finite_abs_bits(float x) {

@@ -7,14 +7,21 @@
 // attention_rows item (the producer quantizes each fresh row); PR
 // description (one scale each for the Lc and Rc rows).
 //
-// One wave64 quantizes one 576-value token row held in registers, so HBM is
-// read once and written once:
+// One wave64 quantizes eight 576-value token rows held in registers, so HBM
+// is read once and written once:
 //   lane l reads Lc[4l..4l+3] and Lc[256+4l..256+4l+3] (two 1 KiB coalesced
-//   float4 loads per wave) and, for l < 16, Rc[4l..4l+3];
-//   the Lc and Rc amax are integer maxima of finite |x| bit patterns reduced
-//   over the wave (exact and order-free);
-//   scale and inverse use correctly rounded f32 division;
-//   each lane packs its 4-value groups into one 32-bit word of codes.
+//   float4 loads per row) and, for l < 16, Rc[4l..4l+3], for all eight rows
+//   before any arithmetic (streaming loads: the source is read once);
+//   the Lc and Rc amax are integer maxima of |x| bit patterns reduced over
+//   the wave with DPP row reductions and four lane reads (exact and
+//   order-free); a segment whose maximum is inf or NaN is reduced again over
+//   its finite values only;
+//   the 2 x 16 correctly rounded divisions (scale and inverse of every
+//   segment) run in one pass, one per lane;
+//   codes come from the gfx950 fp8 conversion (round to nearest even) after
+//   the clamp to [-448, 448] and NaN -> +0, which reproduces the encoder
+//   rules exactly for every f32 value;
+//   the eight scale pairs of a wave are written by eight lanes at once.
 #include "kv8_device.hpp"
 #include "kv8_internal.hpp"
 
@@ -23,64 +30,142 @@
 namespace kv8 {
 namespace {
 
-struct SegScale {
-    float scale;
-    float inv;
-};
-
-// scale = fl32(amax / 448), inv = fl32(448 / amax); guarded (both 0) when the
-// inverse overflows to +inf.
-__device__ __forceinline__ SegScale segment_scale(uint32_t amax_bits) {
-    const float amax = __uint_as_float(amax_bits);
-    const float inv = __fdiv_rn(448.0f, amax);
-    SegScale s;
-    if (__float_as_uint(inv) == 0x7F800000u) {
-        s.scale = 0.0f;
-        s.inv = 0.0f;
-    } else {
-        s.scale = __fdiv_rn(amax, 448.0f);
-        s.inv = inv;
-    }
-    return s;
-}
-
-__device__ __forceinline__ uint32_t encode4(float4 v, float inv) {
-    return pack4(encode_e4m3(__fmul_rn(v.x, inv)), encode_e4m3(__fmul_rn(v.y, inv)),
-                 encode_e4m3(__fmul_rn(v.z, inv)), encode_e4m3(__fmul_rn(v.w, inv)));
-}
-
 __device__ __forceinline__ uint32_t amax4(float4 v) {
     uint32_t a = max(finite_abs_bits(v.x), finite_abs_bits(v.y));
     uint32_t b = max(finite_abs_bits(v.z), finite_abs_bits(v.w));
     return max(a, b);
 }
+// max of |x| bit patterns including inf and NaN (NaN patterns sort above inf)
+__device__ __forceinline__ uint32_t rawmax4(float4 v) {
+    const uint32_t m = 0x7FFFFFFFu;
+    return max(max(__float_as_uint(v.x) & m, __float_as_uint(v.y) & m),
+               max(__float_as_uint(v.z) & m, __float_as_uint(v.w) & m));
+}
 
-constexpr int kQuantWaves = 4;  // rows per 256-thread block
+// Unsigned max over the wave, returned wave-uniform: DPP steps within each
+// row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror), then the four
+// row results read into scalars.
+__device__ __forceinline__ uint32_t wave_max_uniform(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+    const uint32_t r0 = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+    const uint32_t r1 = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+    const uint32_t r3 = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {  // read-once data
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Codes of 4 values q = fl32(x * inv).  `finite` (wave-uniform): the row
+// segment holds no inf or NaN and inv is finite, so q is finite and
+// |q| <= fl32(amax * fl32(448 / amax)) < 464, which round-to-nearest-even
+// takes to at most 448: only the clamp of encode4_e4m3_hw is kept.
+__device__ __forceinline__ uint32_t encode4(float4 v, float inv, bool finite) {
+    const float q0 = __fmul_rn(v.x, inv), q1 = __fmul_rn(v.y, inv);
+    const float q2 = __fmul_rn(v.z, inv), q3 = __fmul_rn(v.w, inv);
+    if (finite) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q0, -448.0f, 448.0f),
+                                                       __builtin_amdgcn_fmed3f(q1, -448.0f, 448.0f), 0, false);
+        return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(
+            __builtin_amdgcn_fmed3f(q2, -448.0f, 448.0f), __builtin_amdgcn_fmed3f(q3, -448.0f, 448.0f), lo, true));
+    }
+    return encode4_e4m3_hw(q0, q1, q2, q3);
+}
+
+constexpr int kQuantWaves = 4;    // waves per 256-thread block
+constexpr int kRowsPerWave = 8;
+constexpr int kSegs = 2 * kRowsPerWave;  // (row, Lc/Rc) segments of a wave
 
 __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     const float* __restrict__ src, int64_t stride, int64_t n_rows,
     uint8_t* __restrict__ codes, float* __restrict__ scales,
     const int64_t* __restrict__ dst_rows) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * kQuantWaves + (threadIdx.x >> 6);
-    if (row >= n_rows) return;
-    const float* x = src + row * stride;
-    const float4 a = *reinterpret_cast<const float4*>(x + 4 * lane);
-    const float4 b = *reinterpret_cast<const float4*>(x + 256 + 4 * lane);
-    float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane < 16) c = *reinterpret_cast<const float4*>(x + kKvLora + 4 * lane);
+    const int64_t row0 =
+        (static_cast<int64_t>(blockIdx.x) * kQuantWaves + (threadIdx.x >> 6)) * kRowsPerWave;
+    if (row0 >= n_rows) return;
+    float4 a[kRowsPerWave], b[kRowsPerWave], c[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        // (a missing second row repeats the first; it is not stored)
+        const int64_t row = row0 + r < n_rows ? row0 + r : row0;
+        const float* x = src + row * stride;
+        a[r] = load_stream(x + 4 * lane);
+        b[r] = load_stream(x + 256 + 4 * lane);
+        c[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lane < 16) c[r] = load_stream(x + kKvLora + 4 * lane);
+    }
 
-    const uint32_t mL = wave_max_u32(max(amax4(a), amax4(b)));
-    const uint32_t mR = wave_max_u32(amax4(c));
-    const SegScale sL = segment_scale(mL);
-    const SegScale sR = segment_scale(mR);
+    // segment k = 2 r + (0: Lc, 1: Rc): amax over finite |x|; the plain
+    // maximum of |x| patterns is that value unless it is inf or NaN
+    uint32_t amax[kSegs];
+    bool finite[kSegs];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        uint32_t mL = wave_max_uniform(max(rawmax4(a[r]), rawmax4(b[r])));
+        uint32_t mR = wave_max_uniform(rawmax4(c[r]));
+        finite[2 * r] = mL < 0x7F800000u;
+        finite[2 * r + 1] = mR < 0x7F800000u;
+        if (!finite[2 * r]) mL = wave_max_uniform(max(amax4(a[r]), amax4(b[r])));
+        if (!finite[2 * r + 1]) mR = wave_max_uniform(amax4(c[r]));
+        amax[2 * r] = mL;
+        amax[2 * r + 1] = mR;
+    }
 
-    const int64_t d = dst_rows ? dst_rows[row] : row;
-    uint8_t* out = codes + d * kRowBytes;
-    reinterpret_cast<uint32_t*>(out)[lane] = encode4(a, sL.inv);
-    reinterpret_cast<uint32_t*>(out + 256)[lane] = encode4(b, sL.inv);
-    if (lane < 16) reinterpret_cast<uint32_t*>(out + kKvLora)[lane] = encode4(c, sR.inv);
-    if (lane == 0) reinterpret_cast<float2*>(scales)[d] = make_float2(sL.scale, sR.scale);
+    // All 2 kSegs correctly rounded divisions in one pass: lane k < kSegs
+    // computes inv_k = 448 / amax_k, lane kSegs + k computes amax_k / 448.
+    const int k = lane & (kSegs - 1);
+    uint32_t am = amax[0];
+#pragma unroll
+    for (int j = 1; j < kSegs; ++j) am = k == j ? amax[j] : am;
+    const bool is_inv = (lane & kSegs) == 0;
+    const float quot = __fdiv_rn(is_inv ? 448.0f : __uint_as_float(am),
+                                 is_inv ? __uint_as_float(am) : 448.0f);
+    float inv[kSegs], scl[kSegs];
+#pragma unroll
+    for (int j = 0; j < kSegs; ++j) {
+        inv[j] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_int(quot), j));
+        scl[j] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_int(quot), kSegs + j));
+        if (__float_as_uint(inv[j]) == 0x7F800000u) {  // guarded: 448 / amax overflows
+            inv[j] = 0.0f;
+            scl[j] = 0.0f;
+            finite[j] = false;
+        }
+    }
+
+    // the wave's scale pairs: lane r < kRowsPerWave holds row r's
+    float2 sp = make_float2(scl[0], scl[1]);
+#pragma unroll
+    for (int r = 1; r < kRowsPerWave; ++r)
+        if (lane == r) sp = make_float2(scl[2 * r], scl[2 * r + 1]);
+    const int64_t nw = n_rows - row0 < kRowsPerWave ? n_rows - row0 : kRowsPerWave;  // rows stored
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        const int64_t row = row0 + r;
+        if (row >= n_rows) break;
+        const int64_t d = dst_rows ? dst_rows[row] : row;
+        uint32_t* out = reinterpret_cast<uint32_t*>(codes + d * kRowBytes);
+        __builtin_nontemporal_store(encode4(a[r], inv[2 * r], finite[2 * r]), out + lane);
+        __builtin_nontemporal_store(encode4(b[r], inv[2 * r], finite[2 * r]), out + 64 + lane);
+        if (lane < 16)
+            __builtin_nontemporal_store(encode4(c[r], inv[2 * r + 1], finite[2 * r + 1]),
+                                        out + kKvLora / 4 + lane);
+        if (dst_rows && r == 0 && lane == 0) reinterpret_cast<float2*>(scales)[d] = sp;
+    }
+    if (dst_rows) {
+        // rows 1.. of a scattered wave: one lane each
+        for (int r = 1; r < nw; ++r)
+            if (lane == r) reinterpret_cast<float2*>(scales)[dst_rows[row0 + r]] = sp;
+    } else if (lane < nw) {
+        reinterpret_cast<float2*>(scales)[row0 + lane] = sp;  // contiguous rows: one store
+    }
 }
 
 // out[k] = encode(f32 with bit pattern first + k), 4 codes per thread.
@@ -90,14 +175,15 @@ __global__ __launch_bounds__(256) void encode_bits_kernel(uint32_t first, uint64
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
          i += static_cast<uint64_t>(gridDim.x) * 256) {
         const uint64_t k = 4 * i;
-        uint32_t c[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            c[j] = encode_e4m3(__uint_as_float(static_cast<uint32_t>(first + k + j)));
+        const uint32_t w = encode4_e4m3_hw(
+            __uint_as_float(static_cast<uint32_t>(first + k)),
+            __uint_as_float(static_cast<uint32_t>(first + k + 1)),
+            __uint_as_float(static_cast<uint32_t>(first + k + 2)),
+            __uint_as_float(static_cast<uint32_t>(first + k + 3)));
         if (k + 4 <= count) {
-            reinterpret_cast<uint32_t*>(out)[i] = pack4(c[0], c[1], c[2], c[3]);
+            reinterpret_cast<uint32_t*>(out)[i] = w;
         } else {
-            for (int j = 0; j < 4 && k + j < count; ++j) out[k + j] = static_cast<uint8_t>(c[j]);
+            for (int j = 0; j < 4 && k + j < count; ++j) out[k + j] = static_cast<uint8_t>(w >> (8 * j));
         }
     }
 }
@@ -121,7 +207,8 @@ __global__ __launch_bounds__(256) void decode_codes_kernel(const uint8_t* __rest
 
 int launch_quantize_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
                          float* scales, const int64_t* dst_rows, hipStream_t stream) {
-    const int64_t blocks = (n_rows + kQuantWaves - 1) / kQuantWaves;
+    const int64_t rows_per_block = static_cast<int64_t>(kQuantWaves) * kRowsPerWave;
+    const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL(quantize_rows_kernel, dim3(static_cast<uint32_t>(blocks)),
                        dim3(64 * kQuantWaves), 0, stream, src, stride, n_rows, codes, scales,
                        dst_rows);

@@ -10,41 +10,44 @@
 // One block = 4 waves = 128 query rows (q, h) of one sequence x one token
 // range.  Wave w owns rows 32w..32w+31 for the whole computation:
 //
-//   tiles of 32 tokens are copied global -> LDS by the direct-to-LDS loads
-//   (three raw fp8 buffers, two tiles in flight); while the MFMAs work on
-//   tile i, all 256 threads decode tile i+1 once, exactly, into an fp16
-//   staging tile (rows padded to 1168 bytes so that the operand reads below
-//   hit distinct banks);
+//   tiles of 32 tokens are copied global -> LDS by direct-to-LDS loads three
+//   tiles ahead (three raw fp8 buffers); two tiles ahead, all 256 threads
+//   decode a raw tile once, exactly, into an fp16 Lc tile (three buffers,
+//   rows padded to 1088 bytes) and turn its scales into (s_Lc, s_Rc,
+//   s_Lc / 2^e); the Rc codes stay in the raw tile;
 //
 //   score pass  S^T[token, row] = dec(KV)[token, 0:576] . q[row, 0:576]
-//               36 MFMA 32x32x16 f16 per tile, A = staged fp16 rows
-//               (ds_read_b128), B = the wave's 32 query rows resident in VGPRs
-//               as fp16 (each row scaled by a power of two so its largest
-//               element sits in [2^14, 2^15): every bf16 input is then exact
-//               in fp16 unless it is 2^32 times smaller than the row maximum);
-//               separate accumulators for the Lc (512) and Rc (64) columns so
-//               the two row scales are applied after the dot product;
+//               36 MFMA 32x32x16 f16 per tile, A = fp16 Lc rows
+//               (ds_read_b128) and the Rc codes converted in registers, B =
+//               the wave's 32 query rows resident in VGPRs as fp16 (each row
+//               scaled by a power of two so its largest element sits in
+//               [2^12, 2^13): every bf16 element above 2^-27 of the row maximum
+//               is then exact in fp16); separate accumulators for the Lc (512)
+//               and Rc (64) columns so the two row scales are applied after the
+//               dot product;
 //
-//   softmax     per row, with weights 2^(c (x - m)), c = softmax_scale log2(e);
-//               a lane holds one row and 16 of the tile's tokens, so row maxima
-//               need one cross-half exchange.  Each row's reference m is its
-//               largest score in the first tile with a visible token and is
-//               only raised when a later tile exceeds it by more than 15 (in
-//               log2 units; p < 2^15 still fits fp16).  Raising it makes the
-//               block finish the pass and run its token range once more with
-//               the final references, so the context accumulator is never
-//               rescaled and lives untouched in AGPRs; the result is the exact
-//               softmax either way;
+//   softmax     per row, with weights 2^(c (x - m)), c = |softmax_scale| log2(e)
+//               (the sign of the softmax scale rides on the row scales); a lane
+//               holds one row and 16 of the tile's tokens, so row maxima need
+//               one cross-half exchange.  Each row's reference m is its largest
+//               score in the first tile with a visible token and is only raised
+//               when a later tile exceeds it by more than 15 (in log2 units;
+//               p < 2^15 still fits fp16).  Raising it makes the block finish
+//               the pass and run its token range once more with the final
+//               references, so the context accumulator is never rescaled and
+//               lives untouched in AGPRs; the result is the exact softmax either
+//               way;
 //
 //   context     O[row, 0:512] += (p * s_Lc / 2^e)[row, token] . dec(Lc)[token, :]
 //               32 MFMA 32x32x16 f16 per tile; the probabilities come straight
 //               from the score accumulator registers (their token order is the
-//               MFMA K order), the staged Lc operand is read with the LDS
-//               transpose load ds_read_b64_tr_b16, and 2^e normalises the largest Lc scale
-//               of the block's token range below 1 so p * s / 2^e fits fp16.
-//               fp16 rather than bf16 carries the probabilities: one bf16
-//               rounding of p already costs ~1e-3 of the output, fp16 ~1e-4,
-//               at the same MFMA rate, and every e4m3 value is exact in fp16.
+//               MFMA K order), the Lc operand is read with the LDS transpose
+//               load ds_read_b64_tr_b16, and 2^e normalises the largest Lc
+//               scale of the block's token range below 1 so p * s / 2^e fits
+//               fp16.  fp16 rather than bf16 carries the probabilities: one
+//               bf16 rounding of p already costs ~1e-3 of the output, fp16
+//               ~1e-4, at the same MFMA rate, and every e4m3 value is exact in
+//               fp16.
 //
 // Both passes therefore run on fp16 MFMA: every e4m3 value and every
 // (row-scaled) bf16 query element is exact in fp16, so the score products are

@@ -305,39 +305,32 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      Copy k < 4 (i < 16, Lc) takes token 2 w + lane / 32 + 8 k, whose
     //      chunk swizzle does not depend on k; copy 4 (i = 16, 17) takes Rc
     //      chunk 2 (i - 16) + lane / 32 of token lane % 32.
-    int dma_lc, dma_rc;
-    {
-        const int t = 2 * w + (lane >> 5);
-        dma_lc = t * kRowBytes + 16 * ((lane & 31) ^ (8 * ((t >> 2) & 1)));
-        dma_rc = (lane & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (lane >> 5));
-    }
-    // copy slot k < kDmaSlots: the wave's code copy k; slot kDmaSlots: the
-    // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (last wave)
+    const int dma_tl = 2 * w + (lane >> 5);  // token of the wave's Lc copy 0
+    const int dma_lc = dma_tl * kRowBytes + 16 * ((lane & 31) ^ (8 * ((dma_tl >> 2) & 1)));
+    const int dma_rc = (lane & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (lane >> 5));
+    // Copy slot k < kDmaSlots: the wave's code copy k; slot kDmaSlots: the
+    // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (last wave).  Tiles
+    // past the range are replaced by the last tile (a harmless re-copy into
+    // a free buffer) so that the pipeline issues copies without branches;
+    // tokens past the range repeat its last row.  The per-lane byte offset
+    // is unsigned and never negative.
     auto issue_copy = [&](int tile, int buf, int k) {
+        tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const int valid = static_cast<int>(te - t0 < kTT ? te - t0 : kTT);
-        if (k < kDmaSlots) {
-            const int i = w + kWaves * k;
-            if (i < kDmaPerTile) {
-                // The per-lane offset is unsigned: it must never go negative.
-                // A full tile folds the first token of copy k (8 k) into the
-                // base; a partial one keeps the tile start as base and clamps
-                // the token past the range to its last row.
-                const int kt = k < 4 ? 8 * k : 0;
-                if (valid == kTT) {
-                    copy_to_lds_b128(p.codes + (row_base + t0 + kt) * kRowBytes,
-                                     k < 4 ? dma_lc : dma_rc, lds_addr(&s_raw[buf][1024 * i]));
-                } else {
-                    int off = (k < 4 ? dma_lc : dma_rc) + kt * kRowBytes;
-                    const int t = off / kRowBytes;
-                    if (t >= valid) off -= (t - (valid - 1)) * kRowBytes;
-                    copy_to_lds_b128(p.codes + (row_base + t0) * kRowBytes, off,
-                                     lds_addr(&s_raw[buf][1024 * i]));
-                }
+        const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
+        if (k < 4) {
+            const int past = max(dma_tl + 8 * k - (valid - 1), 0);
+            copy_to_lds_b128(base, dma_lc + (8 * k - past) * kRowBytes,
+                             lds_addr(&s_raw[buf][1024 * (w + kWaves * k)]));
+        } else if (k == 4) {
+            if (w + kWaves * 4 < kDmaPerTile) {  // waves 0 and 1
+                const int past = max((lane & 31) - (valid - 1), 0);
+                copy_to_lds_b128(base, dma_rc - past * kRowBytes,
+                                 lds_addr(&s_raw[buf][1024 * (w + kWaves * 4)]));
             }
         } else if (w == kWaves - 1) {
-            int tt = lane >> 1;
-            tt = tt < valid ? tt : valid - 1;
+            const int tt = min(lane >> 1, valid - 1);
             copy_to_lds_b32(p.scales + 2 * (row_base + t0), 4 * (2 * tt + (lane & 1)),
                             lds_addr(&s_sc[buf][0]));
         }
@@ -346,18 +339,16 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 #pragma unroll
         for (int k = 0; k <= kDmaSlots; ++k) issue_copy(tile, tile, k);
     };
-    // wait until the copies of an issued tile have landed, `later` tiles
-    // having been issued after it (each wave issues at least 4 copies a tile)
-    auto wait_tile = [&](int later) {
-        if (later >= 2) wait_vmcnt<8>();
-        else if (later == 1) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-    };
+    // wait until the copies of a tile have landed, one tile having been
+    // issued after it (each wave issues at least 4 copies a tile)
+    auto wait_tile = [&]() { wait_vmcnt<4>(); };
 
     // the first three tiles are in flight while the queries load
-    if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
-    if (ntiles > 2) issue_tile(2);
+    if (ntiles > 0) {
+        issue_tile(0);
+        issue_tile(1);
+        issue_tile(2);
+    }
 
     // ---- 2^e above the largest Lc scale of the token range
     uint32_t rbits = 0;
@@ -547,6 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // packed as the A operand of the two context k-steps (phase A)
     uint4 pa[2];
     float mx_part = 0.0f, mx_other = 0.0f, ref = 0.0f, lsum = 0.0f;
+    bool restart = false;  // this lane's row raised its reference in this pass
     auto soft_max_local = [&]() {
         const float m0 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         const float m1 = fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]));
@@ -560,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         const bool first = m_x == mask_val;  // nothing accumulated for this row yet
         const bool raise = !first && c_row * (mx - m_x) > kLazyLog2;
         m_x = real && (first || raise) ? mx : m_x;
-        if (real && raise) s_restart = 1;
+        restart = restart || (real && raise);
         ref = m_x == mask_val ? 0.0f : m_x;
     };
     float4 sev;
@@ -625,13 +617,13 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // Stages past the last tile run on stale buffers and their results are
     // never used.
     for (int attempt = 0; attempt < 2; ++attempt) {
-        if (attempt > 0) {
-            if (ntiles > 0) issue_tile(0);
-            if (ntiles > 1) issue_tile(1);
-            if (ntiles > 2) issue_tile(2);
+        if (attempt > 0 && ntiles > 0) {
+            issue_tile(0);
+            issue_tile(1);
+            issue_tile(2);
         }
         if (ntiles > 0) {
-            wait_tile(ntiles > 2 ? 1 : 0);  // tiles 0 and 1
+            wait_tile();  // tiles 0 and 1
             __syncthreads();
 #pragma unroll
             for (int tile = 0; tile < 2; ++tile) {
@@ -664,7 +656,6 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             const bool real_next = it + 1 < ntiles;
             // ---------------- phase A: score(it + 1), copies of tile it + 3,
             //                  weights of tile it
-            const bool copy = it + 3 < ntiles;
             score_begin(B1);
             lsum = 0.0f;
             order();
@@ -672,9 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             static_for<36>([&](auto kc) {
                 constexpr int ks = decltype(kc)::value;
                 score_step(B1, ks);
-                if constexpr (ks % 6 == 0) {  // one copy every 6 MFMAs
-                    if (copy) issue_copy(it + 3, B0, ks / 6);
-                }
+                if constexpr (ks % 6 == 0) issue_copy(it + 3, B0, ks / 6);  // one copy every 6 MFMAs
                 order();
             });
             mfma_score_drain(accL, accR);
@@ -687,7 +676,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             soft_ref(real_next);
             soft_weights_all(B1);
             l_run += real_next ? lsum : 0.0f;
-            if (it + 2 < ntiles) wait_tile(copy ? 1 : 0);
+            wait_tile();  // tile it + 2
             __syncthreads();
             // ---------------- phase B: context(it), decode(it + 2), the
             //                  reference of tile it + 1
@@ -711,9 +700,13 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             if (it0 + 1 < ntiles) iteration(it0 + 1, std::integral_constant<int, 1>{});
             if (it0 + 2 < ntiles) iteration(it0 + 2, std::integral_constant<int, 2>{});
         }
+        if (restart) s_restart = 1;
+        __syncthreads();
         if (!s_restart) break;
         __syncthreads();
         if (tid == 0) s_restart = 0;
+        restart = false;
+        wait_vmcnt<0>();  // the last re-copies land before the buffers are reused
 #pragma unroll
         for (int dt = 0; dt < 16; ++dt) zero_acc(O[dt]);
         l_run = 0.0f;

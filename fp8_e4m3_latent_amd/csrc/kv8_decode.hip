@@ -260,7 +260,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int g = lane >> 5;        // lane half
     const int l32 = lane & 31;
 
+    // Blocks are dealt round-robin to the 8 XCDs (block i to XCD i % 8);
+    // renumber them so that each XCD runs a contiguous run of logical blocks,
+    // i.e. all token ranges of the same sequences, which then share their
+    // query rows in that XCD's L2.
     int bid = blockIdx.x;
+    if ((gridDim.x & 7) == 0) bid = (bid & 7) * static_cast<int>(gridDim.x >> 3) + (bid >> 3);
     const int rb = bid % p.n_rb;
     bid /= p.n_rb;
     const int split = bid % p.n_splits;
@@ -339,9 +344,6 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 #pragma unroll
         for (int k = 0; k <= kDmaSlots; ++k) issue_copy(tile, tile, k);
     };
-    // wait until the copies of a tile have landed, one tile having been
-    // issued after it (each wave issues at least 4 copies a tile)
-    auto wait_tile = [&]() { wait_vmcnt<4>(); };
 
     // the first three tiles are in flight while the queries load
     if (ntiles > 0) {
@@ -352,8 +354,15 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 
     // ---- 2^e above the largest Lc scale of the token range
     uint32_t rbits = 0;
-    for (int64_t t = ts + tid; t < te; t += kThreads)
-        rbits = max(rbits, __float_as_uint(p.scales[2 * (row_base + t)]));
+    for (int64_t t0 = ts + tid; t0 < te; t0 += 4 * kThreads) {  // four loads in flight
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t t = t0 + u * kThreads;
+            v[u] = t < te ? __float_as_uint(p.scales[2 * (row_base + t)]) : 0u;
+        }
+        rbits = max(rbits, max(max(v[0], v[1]), max(v[2], v[3])));
+    }
 
     // ---- query row l32 of this wave: B operand of the score MFMA, fp16 after
     //      scaling the row by 2^-kq so that its largest magnitude lies in
@@ -610,10 +619,11 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //
     // Software pipeline (tile i): copy(i) is issued three tiles ahead,
     // decode(i) two tiles ahead; iteration i runs
-    //   phase A: score(i + 1), with the copies of tile i + 3 between its
-    //            MFMAs, then the softmax of tile i + 1 (scores, reference,
-    //            weights, packed P')
-    //   phase B: context(i), with decode(i + 2) between its MFMAs
+    //   phase A: score(i + 1), with the copies of tile i + 3 and the decode
+    //            of tile i + 2 between its MFMAs, then the softmax of tile
+    //            i + 1 (scores, reference, weights, packed P')
+    //   phase B: context(i)
+    // and one barrier, after the copies of tile i + 3 have landed.
     // Stages past the last tile run on stale buffers and their results are
     // never used.
     for (int attempt = 0; attempt < 2; ++attempt) {
@@ -623,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             issue_tile(2);
         }
         if (ntiles > 0) {
-            wait_tile();  // tiles 0 and 1
+            wait_vmcnt<0>();  // tiles 0, 1, 2
             __syncthreads();
 #pragma unroll
             for (int tile = 0; tile < 2; ++tile) {
@@ -663,7 +673,15 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             static_for<36>([&](auto kc) {
                 constexpr int ks = decltype(kc)::value;
                 score_step(B1, ks);
-                if constexpr (ks % 6 == 0) issue_copy(it + 3, B0, ks / 6);  // one copy every 6 MFMAs
+                if constexpr (ks <= kDmaSlots) issue_copy(it + 3, B0, ks);
+                // decode of tile it + 2 between the score MFMAs (loads well
+                // ahead of their conversions and stores)
+                if constexpr (ks == 6) decode_load(B2, 0);
+                if constexpr (ks == 7) decode_load(B2, 1);
+                if constexpr (ks >= 12 && ks < 28 && ks % 2 == 0) decode_store(B2, (ks - 12) >> 2, ((ks - 12) >> 1) & 1);
+                if constexpr (ks == 15) decode_load(B2, 2);
+                if constexpr (ks == 19) decode_load(B2, 3);
+                if constexpr (ks == 29) decode_scales(B2);
                 order();
             });
             mfma_score_drain(accL, accR);
@@ -676,23 +694,16 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             soft_ref(real_next);
             soft_weights_all(B1);
             l_run += real_next ? lsum : 0.0f;
-            wait_tile();  // tile it + 2
-            __syncthreads();
-            // ---------------- phase B: context(it), decode(it + 2), the
-            //                  reference of tile it + 1
+            // ---------------- phase B: context(it) (it reads only buffers
+            //                  written before the last barrier)
             context_begin(B0);
             order();
             static_for<32>([&](auto nc) {
                 constexpr int n = decltype(nc)::value;
                 context_step(B0, n, n < 16 ? pa0 : pa1);
-                if constexpr (n == 0) decode_load(B2, 0);
-                if constexpr (n == 1) decode_load(B2, 1);
-                if constexpr (n >= 3 && n < 11) decode_store(B2, (n - 3) >> 1, (n - 3) & 1);
-                if constexpr (n == 4) decode_load(B2, 2);
-                if constexpr (n == 6) decode_load(B2, 3);
-                if constexpr (n == 12) decode_scales(B2);
                 order();
             });
+            wait_vmcnt<0>();  // tile it + 3
             __syncthreads();
         };
         for (int it0 = 0; it0 < ntiles; it0 += kNBuf) {

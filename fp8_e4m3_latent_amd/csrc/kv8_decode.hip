@@ -145,28 +145,49 @@ __device__ __forceinline__ float other_half(float v) {
     return __shfl_xor(v, 32, 64);
 }
 __device__ __forceinline__ float pair_sum(float v) { return v + other_half(v); }
+// max(v, v of lane l ^ 32) with one lane swap between the wave halves (the
+// swap of two copies of v leaves v of the lower half in one copy and v of
+// the upper half in the other, in every lane); no NaN reaches it
+__device__ __forceinline__ float pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return m;
+}
 
 // Score MFMAs with their accumulator pinned to VGPRs, leaving all 256 AGPRs to
-// the context accumulator.  The leading s_nop 1 gives the two wait states a
-// VALU write of an operand needs before an MFMA reads it (the compiler cannot
-// see that the asm is an MFMA); back-to-back MFMAs on the same accumulator
-// need none.  The first MFMA of a chain starts from a zero C operand.
+// the context accumulator.  An MFMA needs two wait states after a VALU
+// write of one of its operands, which the compiler does not insert for
+// inline assembly: the variants taking an operand converted by VALU
+// instructions (NOP = true) start with s_nop 1; the others take operands
+// loaded from LDS (the load's s_waitcnt orders them) or registers written
+// long before.  Back-to-back MFMAs on the same accumulator need no wait
+// state.  The first MFMA of a chain starts from a zero C operand.
+template <bool NOP>
 __device__ __forceinline__ void mfma_score_first(f32x16_t& acc, const f16x8_t& a,
                                                  const f16x8_t& b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+    if constexpr (NOP)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
+template <bool NOP>
 __device__ __forceinline__ void mfma_score(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    if constexpr (NOP)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-// Context MFMA with the accumulator pinned to AGPRs (same hazard note).
+// Context MFMA with the accumulator pinned to AGPRs; its operands are the
+// packed probabilities (written before the phase starts) and LDS loads.
 __device__ __forceinline__ void mfma_ctx(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// Wait states between the last score MFMA and the first VALU read of its
-// accumulator (conservatively more than the result latency).
-__device__ __forceinline__ void mfma_score_drain(f32x16_t& a0, f32x16_t& a1) {
+// Wait states between the last MFMA on an accumulator and the first VALU read
+// of it (conservatively more than the result latency).
+__device__ __forceinline__ void mfma_acc_drain(f32x16_t& a0, f32x16_t& a1) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
 }
 
@@ -190,8 +211,19 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Instruction order inside the software-pipelined phases is fixed in the
 // source: the scheduler cannot see the latency of the asm MFMAs and would
-// otherwise pull loads down next to their uses.
+// otherwise pull loads down next to their uses.  The MFMAs are volatile asm,
+// so they keep their order relative to the LDS and memory instructions;
+// pin(v) (an empty volatile asm reading and writing v) places plain
+// arithmetic: work that depends on a pinned value cannot move above the pin,
+// and a pinned result is computed before it.
 __device__ __forceinline__ void order() { __builtin_amdgcn_sched_barrier(0); }
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;  // (no canonicalisation of the inputs: no NaN reaches the softmax)
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -322,21 +354,35 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     auto issue_copy = [&](int tile, int buf, int k) {
         tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
-        const int valid = static_cast<int>(te - t0 < kTT ? te - t0 : kTT);
         const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
+        const float* sbase = p.scales + 2 * (row_base + t0);
+        if (te - t0 >= kTT) {  // (uniform) a full tile: fixed lane offsets
+            if (k < 4) {
+                copy_to_lds_b128(base + 8 * k * kRowBytes, static_cast<uint32_t>(dma_lc),
+                                 lds_addr(&s_raw[buf][1024 * (w + kWaves * k)]));
+            } else if (k == 4) {
+                if (w + kWaves * 4 < kDmaPerTile)  // waves 0 and 1
+                    copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc),
+                                     lds_addr(&s_raw[buf][1024 * (w + kWaves * 4)]));
+            } else if (w == kWaves - 1) {
+                copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * lane), lds_addr(&s_sc[buf][0]));
+            }
+            return;
+        }
+        const int valid = static_cast<int>(te - t0);
         if (k < 4) {
             const int past = max(dma_tl + 8 * k - (valid - 1), 0);
-            copy_to_lds_b128(base, dma_lc + (8 * k - past) * kRowBytes,
+            copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc + (8 * k - past) * kRowBytes),
                              lds_addr(&s_raw[buf][1024 * (w + kWaves * k)]));
         } else if (k == 4) {
-            if (w + kWaves * 4 < kDmaPerTile) {  // waves 0 and 1
+            if (w + kWaves * 4 < kDmaPerTile) {
                 const int past = max((lane & 31) - (valid - 1), 0);
-                copy_to_lds_b128(base, dma_rc - past * kRowBytes,
+                copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc - past * kRowBytes),
                                  lds_addr(&s_raw[buf][1024 * (w + kWaves * 4)]));
             }
         } else if (w == kWaves - 1) {
             const int tt = min(lane >> 1, valid - 1);
-            copy_to_lds_b32(p.scales + 2 * (row_base + t0), 4 * (2 * tt + (lane & 1)),
+            copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * (2 * tt + (lane & 1))),
                             lds_addr(&s_sc[buf][0]));
         }
     };
@@ -477,13 +523,27 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     };
 
     // x(tile) = s_Lc accL + s_Rc accR for row l32 and tokens 8 (j / 4) + 4 g +
-    // j % 4 of the tile (the accumulator order), masked past the row's limit
+    // j % 4 of the tile (the accumulator order), masked past the row's limit.
+    // The token scales of the lane's 16 tokens are loaded into registers
+    // during the score MFMAs (s_Rc, s_Lc) and before the accumulator drain
+    // (s_Lc / 2^e), so that the softmax does not wait on LDS.
     float x[16];
     f32x16_t accL, accR;
-    auto form_x = [&](int buf, int q4) {
+    float4 sl4[4], sr4[4], se4[4];
+    auto scales_load_l = [&](int buf, int q4) {
+        sl4[q4] = *reinterpret_cast<const float4*>(&s_scd[buf][8 * q4 + 4 * g]);
+    };
+    auto scales_load_r = [&](int buf, int q4) {
+        sr4[q4] = *reinterpret_cast<const float4*>(&s_scd[buf][kTT + 8 * q4 + 4 * g]);
+    };
+    auto scales_load_e = [&](int buf) {
         const float* scd = &s_scd[buf][0];
-        const float4 sl = *reinterpret_cast<const float4*>(scd + 8 * q4 + 4 * g);
-        const float4 sr = *reinterpret_cast<const float4*>(scd + kTT + 8 * q4 + 4 * g);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            se4[q4] = *reinterpret_cast<const float4*>(scd + 2 * kTT + 8 * q4 + 4 * g);
+    };
+    auto form_x = [&](int q4) {
+        const float4 sl = sl4[q4], sr = sr4[q4];
         x[4 * q4 + 0] = __builtin_fmaf(sl.x, accL[4 * q4 + 0], sr.x * accR[4 * q4 + 0]);
         x[4 * q4 + 1] = __builtin_fmaf(sl.y, accL[4 * q4 + 1], sr.y * accR[4 * q4 + 1]);
         x[4 * q4 + 2] = __builtin_fmaf(sl.z, accL[4 * q4 + 2], sr.z * accR[4 * q4 + 2]);
@@ -500,98 +560,140 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         }
     };
 
-    // score(tile): accL = dec(Lc) . q_lat, accR = dec(Rc) . q_rope (36 MFMAs);
-    // one MFMA per step, so that other work can sit between the steps
+    // score(tile): accR = dec(Rc) . q_rope (4 MFMAs, first), then accL =
+    // dec(Lc) . q_lat (32 MFMAs); step ks < 36 issues one MFMA so that other
+    // work can sit between the steps.  The Rc codes of the lane's token are
+    // loaded before the phase (rope_load) and converted one MFMA ahead.
     f16x8_t aq[kScoreAhead];
     uint4 rope[2];
     f16x8_t ropeop;
+    auto rope_load = [&](int buf) {
+        const uint8_t* raw = &s_raw[buf][0];
+        rope[0] = lds_load<uint4>(raw, rope_off);
+        rope[1] = lds_load<uint4>(raw, rope_off + 16 * 32);
+    };
+    auto rope_operand = [&](int r) {
+        const uint4 c4 = rope[r >> 1];
+        ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
+    };
     auto score_begin = [&](int buf) {
         const uint8_t* lc = &s_lc[buf][0];
 #pragma unroll
         for (int k = 0; k < kScoreAhead; ++k)
             aq[k] = lds_load<f16x8_t>(lc, (k & 1 ? sc_base1 : sc_base0) + 64 * (k >> 1));
+        rope_operand(0);
     };
     auto score_step = [&](int buf, int ks) {
         const uint8_t* lc = &s_lc[buf][0];
-        if (ks < 32) {
-            const f16x8_t a = aq[ks % kScoreAhead];
-            const int kn = ks + kScoreAhead;
-            if (kn < 32) aq[ks % kScoreAhead] = lds_load<f16x8_t>(lc, (kn & 1 ? sc_base1 : sc_base0) + 64 * (kn >> 1));
-            if (ks == 20) {  // the Rc codes of the lane's token, two chunks
-                const uint8_t* raw = &s_raw[buf][0];
-                rope[0] = lds_load<uint4>(raw, rope_off);
-                rope[1] = lds_load<uint4>(raw, rope_off + 16 * 32);
-            }
-            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[ks]);
-            if (ks == 0) mfma_score_first(accL, a, qb);
-            else mfma_score(accL, a, qb);
-            if (ks >= 31) {  // Rc operand of the next step
-                const int r = ks - 31;
-                const uint4 c4 = rope[r >> 1];
-                ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
-            }
+        if (ks < 4) {
+            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[32 + ks]);
+            if (ks == 0) mfma_score_first<true>(accR, ropeop, qb);
+            else mfma_score<true>(accR, ropeop, qb);
+            if (ks < 3) rope_operand(ks + 1);
         } else {
-            const int r = ks - 32;
-            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[ks]);
-            if (r == 0) mfma_score_first(accR, ropeop, qb);
-            else mfma_score(accR, ropeop, qb);
-            if (r < 3) {
-                const uint4 c4 = rope[(r + 1) >> 1];
-                ropeop = __builtin_bit_cast(f16x8_t, ((r + 1) & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
-            }
+            const int kl = ks - 4;
+            const f16x8_t a = aq[kl % kScoreAhead];
+            const int kn = kl + kScoreAhead;
+            if (kn < 32) aq[kl % kScoreAhead] = lds_load<f16x8_t>(lc, (kn & 1 ? sc_base1 : sc_base0) + 64 * (kn >> 1));
+            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[kl]);
+            if (kl == 0) mfma_score_first<false>(accL, a, qb);
+            else mfma_score<false>(accL, a, qb);
         }
     };
 
-    // softmax(tile) on x: reference update (phase B, after x), then the
-    // weights p = 2^(c_row (x - ref)), their sum, and fp16 P' = p s_Lc / 2^e
-    // packed as the A operand of the two context k-steps (phase A)
-    uint4 pa[2];
-    float mx_part = 0.0f, mx_other = 0.0f, ref = 0.0f, lsum = 0.0f;
+    // softmax(tile) in steps k < kSoftSteps of a few VALU instructions each,
+    // so that they can sit between the context MFMAs of the previous tile:
+    //   0-8    even k: x of token group k / 2 - 1 (k > 0), then the loads of
+    //          s_Lc and s_Rc for group k / 2 (k < 8); one group of scales in
+    //          flight at a time
+    //   9-10   mask (tiles past the first visible-token limit) and the maximum
+    //          of the lane's 16 scores
+    //   11     the row maximum (with the other half of the wave)
+    //   12     reference update
+    //   13     loads of s_Lc / 2^e for the 16 tokens
+    //   13-20  p = 2^(c_row (x - ref)) for tokens 2 (k - 13) and 2 (k - 13) + 1
+    //   21-24  lsum = sum of the p (pairwise)
+    //   25-28  P' = p s_Lc / 2^e for token group k - 25
+    //   29-30  P' packed to fp16 as the A operand of context k-step k - 29
+    constexpr int kSoftSteps = 31;
+    uint4 pa[2], pn[2];  // P' of the tile in the context MFMAs, and of the next
+    float mx_part = 0.0f, mx_pair = 0.0f, ref = 0.0f, lsum = 0.0f;
+    float mxa = 0.0f, mxb = 0.0f, mxc = 0.0f, sum_t[8];
     bool restart = false;  // this lane's row raised its reference in this pass
-    auto soft_max_local = [&]() {
-        const float m0 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        const float m1 = fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]));
-        const float m2 = fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11]));
-        const float m3 = fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]));
-        mx_part = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-    };
-    auto soft_exchange = [&]() { mx_other = other_half(mx_part); };
-    auto soft_ref = [&](bool real) {
-        const float mx = fmaxf(mx_part, mx_other);
-        const bool first = m_x == mask_val;  // nothing accumulated for this row yet
-        const bool raise = !first && c_row * (mx - m_x) > kLazyLog2;
-        m_x = real && (first || raise) ? mx : m_x;
-        restart = restart || (real && raise);
-        ref = m_x == mask_val ? 0.0f : m_x;
-    };
-    float4 sev;
-    auto soft_scale_load = [&](int buf, int q4) {
-        sev = *reinterpret_cast<const float4*>(&s_scd[buf][2 * kTT + 8 * q4 + 4 * g]);
-    };
-    auto soft_weight = [&](int j) {  // x[j] <- P'[j]
-        const float pj = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
-        lsum += pj;
-        const float se = (j & 3) == 0 ? sev.x : (j & 3) == 1 ? sev.y : (j & 3) == 2 ? sev.z : sev.w;
-        x[j] = pj * se;
-    };
-    auto soft_pack = [&](int kc, int h) {
-        if (h == 0) {
-            pa[kc].x = pack_f16x2(x[8 * kc + 0], x[8 * kc + 1]);
-            pa[kc].y = pack_f16x2(x[8 * kc + 2], x[8 * kc + 3]);
+    auto soft_step = [&](int k, int buf, int tile, bool real) {
+        if (k < 9) {
+            if (k % 2 == 1) return;
+            const int q4 = k / 2;
+            if (q4 > 0) {
+                form_x(q4 - 1);
+                pin(x[4 * q4 - 4]); pin(x[4 * q4 - 3]); pin(x[4 * q4 - 2]); pin(x[4 * q4 - 1]);
+            }
+            if (q4 < 4) {
+                scales_load_l(buf, q4);
+                scales_load_r(buf, q4);
+            }
+            return;
+        }
+        k -= 5;
+        if (k == 4) {
+            mask_x(tile);
+            mxa = max3(x[0], x[1], x[2]);
+            mxb = max3(x[3], x[4], x[5]);
+            mxc = max3(x[6], x[7], x[8]);
+            pin(mxa); pin(mxb); pin(mxc);
+        } else if (k == 5) {
+            const float d = max3(x[9], x[10], x[11]);
+            const float f = max3(x[12], x[13], x[14]);
+            mx_part = fmaxf(max3(mxa, mxb, mxc), max3(d, f, x[15]));
+            pin(mx_part);
+        } else if (k == 6) {
+            mx_pair = pair_max(mx_part);
+            pin(mx_pair);
+        } else if (k == 7) {
+            const float mx = mx_pair;
+            const bool first = m_x == mask_val;  // nothing accumulated for this row yet
+            const bool raise = !first && c_row * (mx - m_x) > kLazyLog2;
+            m_x = real && (first || raise) ? mx : m_x;
+            restart = restart || (real && raise);
+            ref = m_x == mask_val ? 0.0f : m_x;
+            pin(ref);
+        } else if (k < 16) {
+            if (k == 8) scales_load_e(buf);
+            const int j = 2 * (k - 8);
+            pin(x[j]); pin(x[j + 1]);
+            x[j] = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
+            x[j + 1] = __builtin_amdgcn_exp2f(c_row * (x[j + 1] - ref));
+            pin(x[j]); pin(x[j + 1]);
+        } else if (k < 18) {
+            const int j0 = 4 * (k - 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sum_t[j0 + i] = x[2 * (j0 + i)] + x[2 * (j0 + i) + 1];
+                pin(sum_t[j0 + i]);
+            }
+        } else if (k == 18) {
+            sum_t[0] = (sum_t[0] + sum_t[1]) + (sum_t[2] + sum_t[3]);
+            sum_t[4] = (sum_t[4] + sum_t[5]) + (sum_t[6] + sum_t[7]);
+            pin(sum_t[0]); pin(sum_t[4]);
+        } else if (k == 19) {
+            lsum = sum_t[0] + sum_t[4];
+            pin(lsum);
+        } else if (k < 24) {
+            const int q4 = k - 20;
+            pin(x[4 * q4]); pin(x[4 * q4 + 1]); pin(x[4 * q4 + 2]); pin(x[4 * q4 + 3]);
+            x[4 * q4 + 0] *= se4[q4].x;
+            x[4 * q4 + 1] *= se4[q4].y;
+            x[4 * q4 + 2] *= se4[q4].z;
+            x[4 * q4 + 3] *= se4[q4].w;
+            pin(x[4 * q4]); pin(x[4 * q4 + 1]); pin(x[4 * q4 + 2]); pin(x[4 * q4 + 3]);
         } else {
-            pa[kc].z = pack_f16x2(x[8 * kc + 4], x[8 * kc + 5]);
-            pa[kc].w = pack_f16x2(x[8 * kc + 6], x[8 * kc + 7]);
+            const int kc = k - 24;
+            pn[kc].x = pack_f16x2(x[8 * kc + 0], x[8 * kc + 1]);
+            pn[kc].y = pack_f16x2(x[8 * kc + 2], x[8 * kc + 3]);
+            pn[kc].z = pack_f16x2(x[8 * kc + 4], x[8 * kc + 5]);
+            pn[kc].w = pack_f16x2(x[8 * kc + 6], x[8 * kc + 7]);
+            pin(pn[kc].x); pin(pn[kc].y); pin(pn[kc].z); pin(pn[kc].w);
         }
-    };
-    auto soft_weights_all = [&](int tile) {
-        lsum = 0.0f;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            soft_scale_load(tile, q4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) soft_weight(4 * q4 + r);
-        }
-        soft_pack(0, 0); soft_pack(0, 1); soft_pack(1, 0); soft_pack(1, 1);
     };
 
     // context(tile): O[dt] += P (32 rows x 16 tokens) . dec(Lc) (16 tokens x
@@ -620,12 +722,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // Software pipeline (tile i): copy(i) is issued three tiles ahead,
     // decode(i) two tiles ahead; iteration i runs
     //   phase A: score(i + 1), with the copies of tile i + 3 and the decode
-    //            of tile i + 2 between its MFMAs, then the softmax of tile
-    //            i + 1 (scores, reference, weights, packed P')
-    //   phase B: context(i)
-    // and one barrier, after the copies of tile i + 3 have landed.
-    // Stages past the last tile run on stale buffers and their results are
-    // never used.
+    //            of tile i + 2 between its MFMAs
+    //   phase B: context(i), with the softmax steps of tile i + 1 between its
+    //            MFMAs (the P' they pack feeds context(i + 1))
+    // and one barrier, after the copies of tile i + 3 have landed.  Stages
+    // past the last tile run on stale buffers and their results are never
+    // used.
     for (int attempt = 0; attempt < 2; ++attempt) {
         if (attempt > 0 && ntiles > 0) {
             issue_tile(0);
@@ -646,17 +748,14 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 decode_scales(tile);
             }
             __syncthreads();
+            rope_load(0);
             score_begin(0);
             static_for<36>([&](auto ks) { score_step(0, ks); });
-            mfma_score_drain(accL, accR);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) form_x(0, q4);
-            mask_x(0);
-            soft_max_local();
-            soft_exchange();
-            soft_ref(true);
-            soft_weights_all(0);
+            mfma_acc_drain(accL, accR);
+            static_for<kSoftSteps>([&](auto k) { soft_step(decltype(k)::value, 0, 0, true); });
             l_run += lsum;
+            pa[0] = pn[0];
+            pa[1] = pn[1];
         }
         // iteration `it` with R = it % kNBuf known at compile time, so that
         // every LDS address is a lane offset plus an immediate
@@ -665,11 +764,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             constexpr int B0 = R, B1 = (R + 1) % kNBuf, B2 = (R + 2) % kNBuf;
             const bool real_next = it + 1 < ntiles;
             // ---------------- phase A: score(it + 1), copies of tile it + 3,
-            //                  weights of tile it
+            //                  decode of tile it + 2
+            rope_load(B1);
             score_begin(B1);
-            lsum = 0.0f;
             order();
-            const uint4 pa0 = pa[0], pa1 = pa[1];  // P' of tile it
             static_for<36>([&](auto kc) {
                 constexpr int ks = decltype(kc)::value;
                 score_step(B1, ks);
@@ -684,25 +782,21 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 if constexpr (ks == 29) decode_scales(B2);
                 order();
             });
-            mfma_score_drain(accL, accR);
-            // softmax of tile it + 1 (its result is only used when it is real)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) form_x(B1, q4);
-            mask_x(it + 1);
-            soft_max_local();
-            soft_exchange();
-            soft_ref(real_next);
-            soft_weights_all(B1);
-            l_run += real_next ? lsum : 0.0f;
             // ---------------- phase B: context(it) (it reads only buffers
-            //                  written before the last barrier)
+            //                  written before the last barrier), softmax of
+            //                  tile it + 1 (its result is only used when real)
             context_begin(B0);
             order();
             static_for<32>([&](auto nc) {
                 constexpr int n = decltype(nc)::value;
-                context_step(B0, n, n < 16 ? pa0 : pa1);
+                context_step(B0, n, n < 16 ? pa[0] : pa[1]);
+                if constexpr (n == 0) mfma_acc_drain(accL, accR);
+                if constexpr (n < kSoftSteps) soft_step(n, B1, it + 1, real_next);
                 order();
             });
+            l_run += real_next ? lsum : 0.0f;
+            pa[0] = pn[0];
+            pa[1] = pn[1];
             wait_vmcnt<0>();  // tile it + 3
             __syncthreads();
         };

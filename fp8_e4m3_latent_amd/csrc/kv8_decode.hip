@@ -73,12 +73,13 @@ constexpr int kTT = 32;                          // tokens per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 32 * kWaves;       // 128 query rows
-constexpr int kNBuf = 3;                         // raw and decoded tile buffers each
-constexpr int kRawBytes = kTT * kRowBytes;       // 18432: 32 token rows of codes
-constexpr int kRopeRegion = kTT * kKvLora;       // Rc codes start here in a raw tile
+constexpr int kNBuf = 3;                         // raw Lc, decoded and scale buffers each
+constexpr int kRcBufs = 4;                       // raw Rc buffers
+constexpr int kRawLcBytes = kTT * kKvLora;       // 16384: raw Lc codes of a tile
+constexpr int kRawRcBytes = kTT * kRope;         // 2048: raw Rc codes of a tile
 constexpr int kLcStride = 2 * kKvLora + 64;      // 1088: fp16 Lc row + padding
 constexpr int kLcBytes = kTT * kLcStride;        // 34816
-constexpr int kDmaPerTile = kRawBytes / 1024;    // 18 wave-wide 1 KiB copies
+constexpr int kDmaPerTile = (kRawLcBytes + kRawRcBytes) / 1024;  // 18 wave-wide 1 KiB copies
 constexpr int kDmaSlots = (kDmaPerTile + kWaves - 1) / kWaves;  // 5 per wave at most
 constexpr int kScoreAhead = 3;                   // score operand loads in flight
 constexpr int kCtxAhead = 3;                     // context operand loads in flight
@@ -107,6 +108,21 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 16, "vmcnt field");
     __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier after this wave's LDS operations and all of its tile
+// copies except the last N (which stay in flight across the barrier).  The
+// "memory" clobber keeps every LDS access on its side of the barrier; the
+// compiler's own barrier would wait for every copy.
+template <int N>
+__device__ __forceinline__ void barrier_after_copies();
+template <>
+__device__ __forceinline__ void barrier_after_copies<4>() {
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <>
+__device__ __forceinline__ void barrier_after_copies<5>() {
+    asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Direct global -> LDS copies, written as inline assembly.  The compiler then
@@ -268,9 +284,9 @@ __device__ __forceinline__ f16x8_t ctx_operand(const uint8_t* lc, int tb0, int t
 }
 
 // LDS layouts of a tile (32 tokens t; chunks are 16 bytes):
-//   raw    Lc codes of t, chunk q (< 32), at chunk 32 t + (q ^ 8 ((t >> 2) & 1));
-//          Rc codes of t, chunk c (< 4), at chunk 1024 + 32 c + t.  The tile
-//          copies place the chunks there (each lane picks its source chunk).
+//   raw Lc  codes of t, chunk q (< 32), at chunk 32 t + (q ^ 8 ((t >> 2) & 1));
+//   raw Rc  codes of t, chunk c (< 4), at chunk 32 c + t.  The tile copies
+//           place the chunks there (each lane picks its source chunk).
 //   fp16   Lc values of t, chunk c (< 64), at byte 1088 t + 16 (c ^ ((t >> 2) & 3)).
 // With 64 LDS banks of 4 bytes every read and write below touches each bank
 // once per 256 bytes: the score operand reads (16 tokens, one chunk each),
@@ -278,13 +294,16 @@ __device__ __forceinline__ f16x8_t ctx_operand(const uint8_t* lc, int tb0, int t
 // (tokens t and t + 4) and writes (tokens t and t + 4, both chunk parities).
 
 __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kNBuf][kRawBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kNBuf][kRawLcBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_rc[kRcBufs][kRawRcBytes];
     __shared__ __attribute__((aligned(16))) uint8_t s_lc[kNBuf][kLcBytes];
     __shared__ __attribute__((aligned(16))) float s_sc[kNBuf][2 * kTT];   // copied (Lc, Rc) scales
     __shared__ __attribute__((aligned(16))) float s_scd[kNBuf][3 * kTT];  // s_Lc, s_Rc, s_Lc / 2^e
-    __shared__ __attribute__((aligned(16))) float s_row[kWaves][32];
     __shared__ uint32_t s_red[kWaves];
     __shared__ int s_restart;
+    // per-row output factors of the epilogue, in the first raw Lc buffer (no
+    // tile copy or decode is in flight by then)
+    float (*const s_row)[32] = reinterpret_cast<float (*)[32]>(&s_raw[0][0]);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -337,21 +356,25 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int64_t lim_row = n_row < te ? n_row : te;
 
     // ---- tile copies.  Wave w issues the 1 KiB copies i = w + 4k of a tile;
-    //      the 16 bytes of lane l land at raw chunk 64 i + l, whose source
-    //      chunk (token, offset in the token's row) follows the raw layout.
-    //      Copy k < 4 (i < 16, Lc) takes token 2 w + lane / 32 + 8 k, whose
+    //      the 16 bytes of lane l land at chunk 64 i + l of the raw Lc buffer
+    //      (i < 16) or at chunk 64 (i - 16) + l of the raw Rc buffer, whose
+    //      source chunk (token, offset in the token's row) follows the raw
+    //      layouts.  Copy k < 4 (Lc) takes token 2 w + lane / 32 + 8 k, whose
     //      chunk swizzle does not depend on k; copy 4 (i = 16, 17) takes Rc
     //      chunk 2 (i - 16) + lane / 32 of token lane % 32.
     const int dma_tl = 2 * w + (lane >> 5);  // token of the wave's Lc copy 0
     const int dma_lc = dma_tl * kRowBytes + 16 * ((lane & 31) ^ (8 * ((dma_tl >> 2) & 1)));
     const int dma_rc = (lane & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (lane >> 5));
     // Copy slot k < kDmaSlots: the wave's code copy k; slot kDmaSlots: the
-    // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (last wave).  Tiles
-    // past the range are replaced by the last tile (a harmless re-copy into
-    // a free buffer) so that the pipeline issues copies without branches;
-    // tokens past the range repeat its last row.  The per-lane byte offset
-    // is unsigned and never negative.
-    auto issue_copy = [&](int tile, int buf, int k) {
+    // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (last wave).  Tile i
+    // goes to raw Lc and scale buffer lbuf (= i % 3) and raw Rc buffer i % 4.
+    // Tiles past the range are replaced by the last tile (a harmless re-copy
+    // into free buffers) so that the pipeline issues copies without
+    // branches; tokens past the range repeat its last row.  The per-lane byte
+    // offset is unsigned and never negative.  Copies per wave and tile:
+    // waves 0, 1 and 3 issue 5, wave 2 issues 4.
+    auto issue_copy = [&](int tile, int lbuf, int k) {
+        const int rbuf = tile & (kRcBufs - 1);  // (before the clamp)
         tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
@@ -359,13 +382,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         if (te - t0 >= kTT) {  // (uniform) a full tile: fixed lane offsets
             if (k < 4) {
                 copy_to_lds_b128(base + 8 * k * kRowBytes, static_cast<uint32_t>(dma_lc),
-                                 lds_addr(&s_raw[buf][1024 * (w + kWaves * k)]));
+                                 lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
             } else if (k == 4) {
                 if (w + kWaves * 4 < kDmaPerTile)  // waves 0 and 1
-                    copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc),
-                                     lds_addr(&s_raw[buf][1024 * (w + kWaves * 4)]));
+                    copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc), lds_addr(&s_rc[rbuf][1024 * w]));
             } else if (w == kWaves - 1) {
-                copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * lane), lds_addr(&s_sc[buf][0]));
+                copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * lane), lds_addr(&s_sc[lbuf][0]));
             }
             return;
         }
@@ -373,22 +395,22 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         if (k < 4) {
             const int past = max(dma_tl + 8 * k - (valid - 1), 0);
             copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc + (8 * k - past) * kRowBytes),
-                             lds_addr(&s_raw[buf][1024 * (w + kWaves * k)]));
+                             lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
         } else if (k == 4) {
             if (w + kWaves * 4 < kDmaPerTile) {
                 const int past = max((lane & 31) - (valid - 1), 0);
                 copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc - past * kRowBytes),
-                                 lds_addr(&s_raw[buf][1024 * (w + kWaves * 4)]));
+                                 lds_addr(&s_rc[rbuf][1024 * w]));
             }
         } else if (w == kWaves - 1) {
             const int tt = min(lane >> 1, valid - 1);
             copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * (2 * tt + (lane & 1))),
-                            lds_addr(&s_sc[buf][0]));
+                            lds_addr(&s_sc[lbuf][0]));
         }
     };
-    auto issue_tile = [&](int tile) {  // (tile < kNBuf)
+    auto issue_tile = [&](int tile) {  // (tile <= kNBuf)
 #pragma unroll
-        for (int k = 0; k <= kDmaSlots; ++k) issue_copy(tile, tile, k);
+        for (int k = 0; k <= kDmaSlots; ++k) issue_copy(tile, tile % kNBuf, k);
     };
 
     // the first three tiles are in flight while the queries load
@@ -458,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int sc_base0 = l32 * kLcStride + 16 * (g ^ hsw);        // ks even (+64 (ks >> 1))
     const int sc_base1 = l32 * kLcStride + 16 * ((2 + g) ^ hsw);  // ks odd
     // score A operand, Rc: token l32, chunks 2 g and 2 g + 1
-    const int rope_off = kRopeRegion + 16 * (64 * g + l32);
+    const int rope_off = 16 * (64 * g + l32);
     // context B operand: lane (G = lane / 16, gi = lane % 16) of k-group g
     // takes token 4 g + 8 h + gi / 4 (+ 16 kc) at dims 32 dt + 16 (G % 2) +
     // 4 (gi % 4) for its transpose load h
@@ -536,11 +558,8 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     auto scales_load_r = [&](int buf, int q4) {
         sr4[q4] = *reinterpret_cast<const float4*>(&s_scd[buf][kTT + 8 * q4 + 4 * g]);
     };
-    auto scales_load_e = [&](int buf) {
-        const float* scd = &s_scd[buf][0];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            se4[q4] = *reinterpret_cast<const float4*>(scd + 2 * kTT + 8 * q4 + 4 * g);
+    auto scales_load_e = [&](int buf, int q4) {
+        se4[q4] = *reinterpret_cast<const float4*>(&s_scd[buf][2 * kTT + 8 * q4 + 4 * g]);
     };
     auto form_x = [&](int q4) {
         const float4 sl = sl4[q4], sr = sr4[q4];
@@ -567,10 +586,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     f16x8_t aq[kScoreAhead];
     uint4 rope[2];
     f16x8_t ropeop;
-    auto rope_load = [&](int buf) {
-        const uint8_t* raw = &s_raw[buf][0];
-        rope[0] = lds_load<uint4>(raw, rope_off);
-        rope[1] = lds_load<uint4>(raw, rope_off + 16 * 32);
+    auto rope_load = [&](int tile) {
+        const uint8_t* rc = &s_rc[tile & (kRcBufs - 1)][0];
+        rope[0] = lds_load<uint4>(rc, rope_off);
+        rope[1] = lds_load<uint4>(rc, rope_off + 16 * 32);
     };
     auto rope_operand = [&](int r) {
         const uint4 c4 = rope[r >> 1];
@@ -610,9 +629,9 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //          of the lane's 16 scores
     //   11     the row maximum (with the other half of the wave)
     //   12     reference update
-    //   13     loads of s_Lc / 2^e for the 16 tokens
     //   13-20  p = 2^(c_row (x - ref)) for tokens 2 (k - 13) and 2 (k - 13) + 1
-    //   21-24  lsum = sum of the p (pairwise)
+    //   21-24  lsum = sum of the p (pairwise), loads of s_Lc / 2^e for token
+    //          group k - 21
     //   25-28  P' = p s_Lc / 2^e for token group k - 25
     //   29-30  P' packed to fp16 as the A operand of context k-step k - 29
     constexpr int kSoftSteps = 31;
@@ -658,13 +677,13 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             ref = m_x == mask_val ? 0.0f : m_x;
             pin(ref);
         } else if (k < 16) {
-            if (k == 8) scales_load_e(buf);
             const int j = 2 * (k - 8);
             pin(x[j]); pin(x[j + 1]);
             x[j] = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
             x[j + 1] = __builtin_amdgcn_exp2f(c_row * (x[j + 1] - ref));
             pin(x[j]); pin(x[j + 1]);
         } else if (k < 18) {
+            scales_load_e(buf, k - 16);
             const int j0 = 4 * (k - 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -672,10 +691,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 pin(sum_t[j0 + i]);
             }
         } else if (k == 18) {
+            scales_load_e(buf, 2);
             sum_t[0] = (sum_t[0] + sum_t[1]) + (sum_t[2] + sum_t[3]);
             sum_t[4] = (sum_t[4] + sum_t[5]) + (sum_t[6] + sum_t[7]);
             pin(sum_t[0]); pin(sum_t[4]);
         } else if (k == 19) {
+            scales_load_e(buf, 3);
             lsum = sum_t[0] + sum_t[4];
             pin(lsum);
         } else if (k < 24) {
@@ -719,15 +740,20 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // kLazyLog2 of every tile maximum) and the range is then run once more
     // from a zero accumulator.
     //
-    // Software pipeline (tile i): copy(i) is issued three tiles ahead,
-    // decode(i) two tiles ahead; iteration i runs
-    //   phase A: score(i + 1), with the copies of tile i + 3 and the decode
-    //            of tile i + 2 between its MFMAs
-    //   phase B: context(i), with the softmax steps of tile i + 1 between its
-    //            MFMAs (the P' they pack feeds context(i + 1))
+    // Software pipeline (tile i): copy(i) is issued four tiles ahead and
+    // waited for at the end of the next iteration, decode(i) runs two tiles
+    // ahead; iteration i runs
+    //   phase A: score(i + 1), with the decode of tile i + 2 between its MFMAs
+    //   phase B: context(i), with the softmax steps of tile i + 1 (the P'
+    //            they pack feeds context(i + 1)) and the copies of tile i + 4
+    //            between its MFMAs
     // and one barrier, after the copies of tile i + 3 have landed.  Stages
     // past the last tile run on stale buffers and their results are never
     // used.
+    auto end_barrier = [&]() {
+        if (w == 2) barrier_after_copies<4>();
+        else barrier_after_copies<5>();
+    };
     for (int attempt = 0; attempt < 2; ++attempt) {
         if (attempt > 0 && ntiles > 0) {
             issue_tile(0);
@@ -748,6 +774,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 decode_scales(tile);
             }
             __syncthreads();
+            issue_tile(3);  // (raw buffers of tile 0, decoded)
             rope_load(0);
             score_begin(0);
             static_for<36>([&](auto ks) { score_step(0, ks); });
@@ -756,6 +783,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             l_run += lsum;
             pa[0] = pn[0];
             pa[1] = pn[1];
+            end_barrier();  // tile 0's Rc codes are read before copy(4) reuses them
         }
         // iteration `it` with R = it % kNBuf known at compile time, so that
         // every LDS address is a lane offset plus an immediate
@@ -763,28 +791,27 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             constexpr int R = decltype(rc)::value;
             constexpr int B0 = R, B1 = (R + 1) % kNBuf, B2 = (R + 2) % kNBuf;
             const bool real_next = it + 1 < ntiles;
-            // ---------------- phase A: score(it + 1), copies of tile it + 3,
-            //                  decode of tile it + 2
-            rope_load(B1);
+            // ---------------- phase A: score(it + 1), decode of tile it + 2
+            rope_load(it + 1);
             score_begin(B1);
             order();
             static_for<36>([&](auto kc) {
                 constexpr int ks = decltype(kc)::value;
                 score_step(B1, ks);
-                if constexpr (ks <= kDmaSlots) issue_copy(it + 3, B0, ks);
                 // decode of tile it + 2 between the score MFMAs (loads well
                 // ahead of their conversions and stores)
-                if constexpr (ks == 6) decode_load(B2, 0);
-                if constexpr (ks == 7) decode_load(B2, 1);
-                if constexpr (ks >= 12 && ks < 28 && ks % 2 == 0) decode_store(B2, (ks - 12) >> 2, ((ks - 12) >> 1) & 1);
-                if constexpr (ks == 15) decode_load(B2, 2);
-                if constexpr (ks == 19) decode_load(B2, 3);
-                if constexpr (ks == 29) decode_scales(B2);
+                if constexpr (ks >= 6 && ks <= 30 && (ks - 6) % 8 == 0) decode_load(B2, (ks - 6) / 8);
+                if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(B2, (ks - 9) / 8, 0);
+                if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(B2, (ks - 11) / 8, 1);
+                if constexpr (ks == 35) decode_scales(B2);
                 order();
             });
             // ---------------- phase B: context(it) (it reads only buffers
             //                  written before the last barrier), softmax of
-            //                  tile it + 1 (its result is only used when real)
+            //                  tile it + 1 (its result is only used when real),
+            //                  copies of tile it + 4 into the buffers of tile
+            //                  it + 1 (raw Lc, scales: decoded last iteration)
+            //                  and tile it (raw Rc: scored last iteration)
             context_begin(B0);
             order();
             static_for<32>([&](auto nc) {
@@ -792,13 +819,13 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 context_step(B0, n, n < 16 ? pa[0] : pa[1]);
                 if constexpr (n == 0) mfma_acc_drain(accL, accR);
                 if constexpr (n < kSoftSteps) soft_step(n, B1, it + 1, real_next);
+                if constexpr (n % 4 == 1 && n / 4 <= kDmaSlots) issue_copy(it + 4, B1, n / 4);
                 order();
             });
             l_run += real_next ? lsum : 0.0f;
             pa[0] = pn[0];
             pa[1] = pn[1];
-            wait_vmcnt<0>();  // tile it + 3
-            __syncthreads();
+            end_barrier();  // tile it + 3 landed; tile it + 4 may be in flight
         };
         for (int it0 = 0; it0 < ntiles; it0 += kNBuf) {
             iteration(it0, std::integral_constant<int, 0>{});

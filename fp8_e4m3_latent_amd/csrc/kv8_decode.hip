@@ -80,7 +80,7 @@ constexpr int kRawRcBytes = kTT * kRope;         // 2048: raw Rc codes of a tile
 constexpr int kLcStride = 2 * kKvLora + 64;      // 1088: fp16 Lc row + padding
 constexpr int kLcBytes = kTT * kLcStride;        // 34816
 constexpr int kDmaPerTile = (kRawLcBytes + kRawRcBytes) / 1024;  // 18 wave-wide 1 KiB copies
-constexpr int kDmaSlots = (kDmaPerTile + kWaves - 1) / kWaves;  // 5 per wave at most
+constexpr int kCopiesPerTile = 6;                // per wave: 4 Lc, 1 Rc, 1 scales
 constexpr int kScoreAhead = 3;                   // score operand loads in flight
 constexpr int kCtxAhead = 3;                     // context operand loads in flight
 constexpr float kLazyLog2 = 15.0f;
@@ -117,12 +117,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int N>
 __device__ __forceinline__ void barrier_after_copies();
 template <>
-__device__ __forceinline__ void barrier_after_copies<4>() {
-    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-template <>
-__device__ __forceinline__ void barrier_after_copies<5>() {
-    asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void barrier_after_copies<6>() {
+    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Direct global -> LDS copies, written as inline assembly.  The compiler then
@@ -365,53 +361,45 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int dma_tl = 2 * w + (lane >> 5);  // token of the wave's Lc copy 0
     const int dma_lc = dma_tl * kRowBytes + 16 * ((lane & 31) ^ (8 * ((dma_tl >> 2) & 1)));
     const int dma_rc = (lane & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (lane >> 5));
-    // Copy slot k < kDmaSlots: the wave's code copy k; slot kDmaSlots: the
-    // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (last wave).  Tile i
-    // goes to raw Lc and scale buffer lbuf (= i % 3) and raw Rc buffer i % 4.
-    // Tiles past the range are replaced by the last tile (a harmless re-copy
-    // into free buffers) so that the pipeline issues copies without
-    // branches; tokens past the range repeat its last row.  The per-lane byte
-    // offset is unsigned and never negative.  Copies per wave and tile:
-    // waves 0, 1 and 3 issue 5, wave 2 issues 4.
-    auto issue_copy = [&](int tile, int lbuf, int k) {
+    // The copies of a tile: tile i goes to raw Lc and scale buffer lbuf
+    // (= i % 3) and raw Rc buffer i % 4.  Every wave issues the same
+    // kCopiesPerTile copies (no branch on the wave): its four Lc copies, one Rc
+    // copy (waves w and w + 2 copy the same Rc chunks; the duplicate writes
+    // carry identical bytes) and the tile's 32 (Lc, Rc) scale pairs, 4 bytes
+    // per lane (every wave the same 256 bytes).  Tiles past the range are
+    // replaced by the last tile (a harmless re-copy into free buffers);
+    // tokens past the range repeat its last row.  The per-lane byte offset is
+    // unsigned and never negative.
+    auto issue_tile_copies = [&](int tile, int lbuf) {
         const int rbuf = tile & (kRcBufs - 1);  // (before the clamp)
         tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
         const float* sbase = p.scales + 2 * (row_base + t0);
+        const uint32_t rc_lds = lds_addr(&s_rc[rbuf][1024 * (w & 1)]);
         if (te - t0 >= kTT) {  // (uniform) a full tile: fixed lane offsets
-            if (k < 4) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
                 copy_to_lds_b128(base + 8 * k * kRowBytes, static_cast<uint32_t>(dma_lc),
                                  lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
-            } else if (k == 4) {
-                if (w + kWaves * 4 < kDmaPerTile)  // waves 0 and 1
-                    copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc), lds_addr(&s_rc[rbuf][1024 * w]));
-            } else if (w == kWaves - 1) {
-                copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * lane), lds_addr(&s_sc[lbuf][0]));
+            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc), rc_lds);
+            copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * lane), lds_addr(&s_sc[lbuf][0]));
+        } else {
+            const int valid = static_cast<int>(te - t0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int past = max(dma_tl + 8 * k - (valid - 1), 0);
+                copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc + (8 * k - past) * kRowBytes),
+                                 lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
             }
-            return;
-        }
-        const int valid = static_cast<int>(te - t0);
-        if (k < 4) {
-            const int past = max(dma_tl + 8 * k - (valid - 1), 0);
-            copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc + (8 * k - past) * kRowBytes),
-                             lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
-        } else if (k == 4) {
-            if (w + kWaves * 4 < kDmaPerTile) {
-                const int past = max((lane & 31) - (valid - 1), 0);
-                copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc - past * kRowBytes),
-                                 lds_addr(&s_rc[rbuf][1024 * w]));
-            }
-        } else if (w == kWaves - 1) {
+            const int past = max((lane & 31) - (valid - 1), 0);
+            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc - past * kRowBytes), rc_lds);
             const int tt = min(lane >> 1, valid - 1);
             copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * (2 * tt + (lane & 1))),
                             lds_addr(&s_sc[lbuf][0]));
         }
     };
-    auto issue_tile = [&](int tile) {  // (tile <= kNBuf)
-#pragma unroll
-        for (int k = 0; k <= kDmaSlots; ++k) issue_copy(tile, tile % kNBuf, k);
-    };
+    auto issue_tile = [&](int tile) { issue_tile_copies(tile, tile % kNBuf); };
 
     // the first three tiles are in flight while the queries load
     if (ntiles > 0) {
@@ -533,15 +521,15 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         const uint4 v = half == 0 ? dec8_f16(r.x, r.y) : dec8_f16(r.z, r.w);
         *reinterpret_cast<uint4*>(lc + (half == 0 ? d_wA : (d_wA ^ 16)) + 256 * j) = v;
     };
+    // (every wave writes the same values: lane t < 32 the signed s_Lc, s_Rc
+    // of token t, lane 32 + t the value s_Lc / 2^e of token t, twice)
     auto decode_scales = [&](int buf) {
-        if (tid < kTT) {
-            const float sl = s_sc[buf][2 * tid];
-            const float sr = s_sc[buf][2 * tid + 1];
-            float* d = &s_scd[buf][0];
-            d[tid] = sgn * sl;
-            d[kTT + tid] = sgn * sr;
-            d[2 * kTT + tid] = __builtin_ldexpf(sl, -e);
-        }
+        const float2 sc = *reinterpret_cast<const float2*>(&s_sc[buf][2 * l32]);
+        float* d = &s_scd[buf][0];
+        const float v0 = g == 0 ? sgn * sc.x : __builtin_ldexpf(sc.x, -e);
+        const float v1 = g == 0 ? sgn * sc.y : v0;
+        d[g == 0 ? l32 : 2 * kTT + l32] = v0;
+        d[g == 0 ? kTT + l32 : 2 * kTT + l32] = v1;
     };
 
     // x(tile) = s_Lc accL + s_Rc accR for row l32 and tokens 8 (j / 4) + 4 g +
@@ -743,17 +731,14 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // Software pipeline (tile i): copy(i) is issued four tiles ahead and
     // waited for at the end of the next iteration, decode(i) runs two tiles
     // ahead; iteration i runs
-    //   phase A: score(i + 1), with the decode of tile i + 2 between its MFMAs
-    //   phase B: context(i), with the softmax steps of tile i + 1 (the P'
-    //            they pack feeds context(i + 1)) and the copies of tile i + 4
-    //            between its MFMAs
+    //   phase A: score(i + 1), with the decode of tile i + 2 and the copies
+    //            of tile i + 4 between its MFMAs
+    //   phase B: context(i), with the softmax steps of tile i + 1 between its
+    //            MFMAs (the P' they pack feeds context(i + 1))
     // and one barrier, after the copies of tile i + 3 have landed.  Stages
     // past the last tile run on stale buffers and their results are never
     // used.
-    auto end_barrier = [&]() {
-        if (w == 2) barrier_after_copies<4>();
-        else barrier_after_copies<5>();
-    };
+    auto end_barrier = [&]() { barrier_after_copies<kCopiesPerTile>(); };
     for (int attempt = 0; attempt < 2; ++attempt) {
         if (attempt > 0 && ntiles > 0) {
             issue_tile(0);
@@ -791,7 +776,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             constexpr int R = decltype(rc)::value;
             constexpr int B0 = R, B1 = (R + 1) % kNBuf, B2 = (R + 2) % kNBuf;
             const bool real_next = it + 1 < ntiles;
-            // ---------------- phase A: score(it + 1), decode of tile it + 2
+            // ---------------- phase A: score(it + 1), decode of tile it + 2,
+            //                  copies of tile it + 4 into the buffers of tile
+            //                  it + 1 (raw Lc, scales: decoded last iteration)
+            //                  and tile it (raw Rc: scored last iteration)
             rope_load(it + 1);
             score_begin(B1);
             order();
@@ -804,14 +792,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(B2, (ks - 9) / 8, 0);
                 if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(B2, (ks - 11) / 8, 1);
                 if constexpr (ks == 35) decode_scales(B2);
+                if constexpr (ks == 2) issue_tile_copies(it + 4, B1);
                 order();
             });
             // ---------------- phase B: context(it) (it reads only buffers
             //                  written before the last barrier), softmax of
-            //                  tile it + 1 (its result is only used when real),
-            //                  copies of tile it + 4 into the buffers of tile
-            //                  it + 1 (raw Lc, scales: decoded last iteration)
-            //                  and tile it (raw Rc: scored last iteration)
+            //                  tile it + 1 (its result is only used when real)
             context_begin(B0);
             order();
             static_for<32>([&](auto nc) {
@@ -819,7 +805,6 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 context_step(B0, n, n < 16 ? pa[0] : pa[1]);
                 if constexpr (n == 0) mfma_acc_drain(accL, accR);
                 if constexpr (n < kSoftSteps) soft_step(n, B1, it + 1, real_next);
-                if constexpr (n % 4 == 1 && n / 4 <= kDmaSlots) issue_copy(it + 4, B1, n / 4);
                 order();
             });
             l_run += real_next ? lsum : 0.0f;

@@ -80,7 +80,7 @@ constexpr int kRawRcBytes = kTT * kRope;         // 2048: raw Rc codes of a tile
 constexpr int kLcStride = 2 * kKvLora + 64;      // 1088: fp16 Lc row + padding
 constexpr int kLcBytes = kTT * kLcStride;        // 34816
 constexpr int kDmaPerTile = (kRawLcBytes + kRawRcBytes) / 1024;  // 18 wave-wide 1 KiB copies
-constexpr int kCopiesPerTile = 6;                // per wave: 4 Lc, 1 Rc, 1 scales
+
 constexpr int kScoreAhead = 3;                   // score operand loads in flight
 constexpr int kCtxAhead = 3;                     // context operand loads in flight
 constexpr float kLazyLog2 = 15.0f;
@@ -117,8 +117,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int N>
 __device__ __forceinline__ void barrier_after_copies();
 template <>
-__device__ __forceinline__ void barrier_after_copies<6>() {
-    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void barrier_after_copies<4>() {
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <>
+__device__ __forceinline__ void barrier_after_copies<5>() {
+    asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Direct global -> LDS copies, written as inline assembly.  The compiler then
@@ -318,6 +322,22 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int split = bid % p.n_splits;
     const int b = bid / p.n_splits;
 
+    // the query rows load first: they do not depend on the cache layout, and
+    // the tile copies, the scale loads and these complete together
+    const int row0 = rb * kRowsPerBlock;
+    const int row = row0 + 32 * w + l32;
+    const bool row_ok = row < p.QH;
+    uint4 qv[36];
+    {
+        const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
+        const uint4* ql = reinterpret_cast<const uint4*>(p.q_lat + qrow * kKvLora);
+        const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) qv[ks] = ql[2 * ks + g];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qv[32 + r] = qr[4 * g + r];
+    }
+
     const int64_t L = p.kv_len[b];
     const int64_t row_base = p.kv_start[b];
     int64_t ts, te;
@@ -337,7 +357,6 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     }
     te = L < te ? L : te;
 
-    const int row0 = rb * kRowsPerBlock;
     const int row_hi = (p.QH < row0 + kRowsPerBlock ? p.QH : row0 + kRowsPerBlock) - 1;
     const int64_t n_first = L - (p.Q - 1) + row0 / p.H;    // visible tokens, first row
     const int64_t n_last = L - (p.Q - 1) + row_hi / p.H;   // visible tokens, last row
@@ -346,8 +365,6 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int ntiles = static_cast<int>((ntok + kTT - 1) / kTT);
     const int64_t full_until = te < n_first ? te : n_first;  // no mask below this token
 
-    const int row = row0 + 32 * w + l32;
-    const bool row_ok = row < p.QH;
     const int64_t n_row = row_ok ? L - (p.Q - 1) + row / p.H : 0;
     const int64_t lim_row = n_row < te ? n_row : te;
 
@@ -362,44 +379,39 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int dma_lc = dma_tl * kRowBytes + 16 * ((lane & 31) ^ (8 * ((dma_tl >> 2) & 1)));
     const int dma_rc = (lane & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (lane >> 5));
     // The copies of a tile: tile i goes to raw Lc and scale buffer lbuf
-    // (= i % 3) and raw Rc buffer i % 4.  Every wave issues the same
-    // kCopiesPerTile copies (no branch on the wave): its four Lc copies, one Rc
-    // copy (waves w and w + 2 copy the same Rc chunks; the duplicate writes
-    // carry identical bytes) and the tile's 32 (Lc, Rc) scale pairs, 4 bytes
-    // per lane (every wave the same 256 bytes).  Tiles past the range are
-    // replaced by the last tile (a harmless re-copy into free buffers);
-    // tokens past the range repeat its last row.  The per-lane byte offset is
-    // unsigned and never negative.
-    auto issue_tile_copies = [&](int tile, int lbuf) {
+    // (= i % 3) and raw Rc buffer i % 4.  Copy slot k < 4 of wave w is its Lc
+    // copy k; slot 4 is the Rc copy of wave w (waves 0 and 1) or the tile's 32
+    // (Lc, Rc) scale pairs, 4 bytes per lane (wave 3): waves 0, 1 and 3 issue
+    // five copies per tile, wave 2 four.  Tiles past the range are replaced
+    // by the last tile (a harmless re-copy into free buffers); tokens past
+    // the range repeat its last row.  The per-lane byte offset is unsigned and
+    // never negative.
+    auto issue_copy = [&](int tile, int lbuf, int k) {
         const int rbuf = tile & (kRcBufs - 1);  // (before the clamp)
         tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
         const float* sbase = p.scales + 2 * (row_base + t0);
-        const uint32_t rc_lds = lds_addr(&s_rc[rbuf][1024 * (w & 1)]);
-        if (te - t0 >= kTT) {  // (uniform) a full tile: fixed lane offsets
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                copy_to_lds_b128(base + 8 * k * kRowBytes, static_cast<uint32_t>(dma_lc),
-                                 lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
-            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc), rc_lds);
-            copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * lane), lds_addr(&s_sc[lbuf][0]));
-        } else {
-            const int valid = static_cast<int>(te - t0);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int past = max(dma_tl + 8 * k - (valid - 1), 0);
-                copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc + (8 * k - past) * kRowBytes),
-                                 lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
-            }
-            const int past = max((lane & 31) - (valid - 1), 0);
-            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc - past * kRowBytes), rc_lds);
-            const int tt = min(lane >> 1, valid - 1);
+        const bool full = te - t0 >= kTT;  // (uniform) fixed lane offsets
+        const int valid = static_cast<int>(full ? kTT : te - t0);
+        if (k < 4) {
+            const int past = full ? 0 : max(dma_tl + 8 * k - (valid - 1), 0);
+            copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc + (8 * k - past) * kRowBytes),
+                             lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
+        } else if (w < 2) {
+            const int past = full ? 0 : max((lane & 31) - (valid - 1), 0);
+            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc - past * kRowBytes),
+                             lds_addr(&s_rc[rbuf][1024 * w]));
+        } else if (w == 3) {
+            const int tt = full ? (lane >> 1) : min(lane >> 1, valid - 1);
             copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * (2 * tt + (lane & 1))),
                             lds_addr(&s_sc[lbuf][0]));
         }
     };
-    auto issue_tile = [&](int tile) { issue_tile_copies(tile, tile % kNBuf); };
+    auto issue_tile = [&](int tile) {
+#pragma unroll
+        for (int k = 0; k < 5; ++k) issue_copy(tile, tile % kNBuf, k);
+    };
 
     // the first three tiles are in flight while the queries load
     if (ntiles > 0) {
@@ -427,16 +439,8 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      Rc k-step r holds rope columns 32 g + 8 r .. +8 (the Rc operand
     //      below takes the same order).  Rows past Q*H (block padding) reuse
     //      row 0; their results are never stored.
-    uint4 qv[36];
     int kq = 0;
     {
-        const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
-        const uint4* ql = reinterpret_cast<const uint4*>(p.q_lat + qrow * kKvLora);
-        const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) qv[ks] = ql[2 * ks + g];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) qv[32 + r] = qr[4 * g + r];
         uint32_t mbits = 0;
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks)
@@ -504,9 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 
     f32x16_t O[16];
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) O[dt][j] = 0.0f;
+    for (int dt = 0; dt < 16; ++dt) zero_acc(O[dt]);
 
     // ---- pipeline stages --------------------------------------------------
     // decode(tile): raw codes -> fp16 Lc tile, scales -> (s_Lc, s_Rc, s_Lc/2^e)
@@ -731,14 +733,19 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // Software pipeline (tile i): copy(i) is issued four tiles ahead and
     // waited for at the end of the next iteration, decode(i) runs two tiles
     // ahead; iteration i runs
-    //   phase A: score(i + 1), with the decode of tile i + 2 and the copies
-    //            of tile i + 4 between its MFMAs
+    //   phase A: score(i + 1), with the decode of tile i + 2 between its
+    //            MFMAs
     //   phase B: context(i), with the softmax steps of tile i + 1 between its
     //            MFMAs (the P' they pack feeds context(i + 1))
+    // and the five copy slots of tile i + 4 spread over both phases (a burst
+    // of copies stalls their issue while earlier misses are outstanding)
     // and one barrier, after the copies of tile i + 3 have landed.  Stages
     // past the last tile run on stale buffers and their results are never
     // used.
-    auto end_barrier = [&]() { barrier_after_copies<kCopiesPerTile>(); };
+    auto end_barrier = [&]() {
+        if (w == 2) barrier_after_copies<4>();
+        else barrier_after_copies<5>();
+    };
     for (int attempt = 0; attempt < 2; ++attempt) {
         if (attempt > 0 && ntiles > 0) {
             issue_tile(0);
@@ -792,7 +799,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(B2, (ks - 9) / 8, 0);
                 if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(B2, (ks - 11) / 8, 1);
                 if constexpr (ks == 35) decode_scales(B2);
-                if constexpr (ks == 2) issue_tile_copies(it + 4, B1);
+                if constexpr (ks % 11 == 3) issue_copy(it + 4, B1, ks / 11);
                 order();
             });
             // ---------------- phase B: context(it) (it reads only buffers
@@ -805,6 +812,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 context_step(B0, n, n < 16 ? pa[0] : pa[1]);
                 if constexpr (n == 0) mfma_acc_drain(accL, accR);
                 if constexpr (n < kSoftSteps) soft_step(n, B1, it + 1, real_next);
+                if constexpr (n % 11 == 5 && n / 11 < 2) issue_copy(it + 4, B1, 3 + n / 11);
                 order();
             });
             l_run += real_next ? lsum : 0.0f;

@@ -14,7 +14,9 @@ latent rows of 512 Lc + 64 Rc e4m3 codes with per-row f32 scales.  Each step
 Three copies of the cache (3 x 153 MB, more than the 256 MB last-level cache)
 are used in rotation so every step reads its KV from HBM.  Inputs are resident
 in HBM before the timed region; times come from HIP events on the stream the
-kernels run on.
+kernels run on.  The decode kernel's roofline uses its duration over launches
+of that kernel alone, back to back on the same rotating caches (the per-step
+events around it also hold its dispatch gap behind the append kernel).
 
 Other legs (same JSON line, key "legs"): the bulk quantizer (32,768 tokens x
 61 layers of Student-t rows with planted special rows), the 256k-token
@@ -150,6 +152,21 @@ def leg_decode(torch, kv8, W, steps, warmup, cpu_sample_rows):
                       "absorb_decode_kernel_best": float(iv[:, 1].min())},
         "flops_per_step": flops, "kv_bytes_per_step": kv_bytes,
     }
+    # duration of the decode kernel alone for the roofline: the same launches
+    # back to back (the per-step events above also hold each launch's
+    # dispatch gap behind the append kernel)
+    b2b = max(steps, 10)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(b2b):
+        c = (warmup + steps + i) % n_copies
+        kv8.absorb_decode_partials(qs[c][0], qs[c][1], caches[c][0], caches[c][1], kv_start, kv_len,
+                                   T, sc, split_tokens, n_splits, partials)
+    e1.record()
+    torch.cuda.synchronize()
+    res["kernel_ms"]["absorb_decode_kernel_back_to_back"] = e0.elapsed_time(e1) / b2b
     res["decode_kernel_tflops"] = flops / (dec_ms * 1e-3) / 1e12
     res["decode_kernel_kv_gb_per_s"] = kv_bytes / (dec_ms * 1e-3) / 1e9
     # CPU baseline: the oracle on a bounded sample of the same decode
@@ -301,9 +318,9 @@ def main():
 
     res, cpu = leg_decode(torch, kv8, W, args.steps, args.warmup, args.cpu_sample_rows)
     flops = res["flops_per_step"]
-    dec_ms = res["kernel_ms"]["absorb_decode_kernel"]
+    dec_ms = res["kernel_ms"]["absorb_decode_kernel_back_to_back"]
     ach = flops / (dec_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": "absorb_decode_kernel",
+    roof = {"bound": "mfma", "kernel": "absorb_decode_kernel", "kernel_ms": dec_ms,
             "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": ach / PEAK_BF16_TFLOPS,
             "traffic": counter_traffic("absorb_decode_kernel", "kv8_decode.hip")}

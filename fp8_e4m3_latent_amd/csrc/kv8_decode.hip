@@ -110,6 +110,30 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// Wait for every copy and load of this wave in flight; also a compiler
+// memory barrier, so that LDS reads of copied data stay after it.
+__device__ __forceinline__ void wait_all_copies() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// The lane id from an instruction that the compiler can neither hoist nor
+// merge.  Copy offsets computed from it are rebuilt where they are used
+// instead of being kept live (and possibly spilled: a scratch reload waits
+// for every copy in flight).
+__device__ __forceinline__ int fresh_lane_id() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// A load through the constant address space: with a uniform address it is a
+// scalar load, counted by lgkmcnt, so waiting for it does not wait for the
+// vector loads and copies in flight.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* ptr) {
+    return *(const __attribute__((address_space(4))) T*)(ptr);
+}
+
 // Workgroup barrier after this wave's LDS operations and all of its tile
 // copies except the last N (which stay in flight across the barrier).  The
 // "memory" clobber keeps every LDS access on its side of the barrier; the
@@ -322,24 +346,38 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int split = bid % p.n_splits;
     const int b = bid / p.n_splits;
 
-    // the query rows load first: they do not depend on the cache layout, and
-    // the tile copies, the scale loads and these complete together
     const int row0 = rb * kRowsPerBlock;
     const int row = row0 + 32 * w + l32;
     const bool row_ok = row < p.QH;
+
+    const int64_t L = load_uniform(p.kv_len + b);
+    const int64_t row_base = load_uniform(p.kv_start + b);
+
+    // ---- query rows of this wave.  In the MFMA operand order every load
+    //      would touch 32 rows (32 bytes of each), so the 32 latent rows
+    //      (1 KiB each) are copied whole into LDS first, one row per copy, and
+    //      read back in operand order once they have landed.  Lane l of the
+    //      copy of row j takes the row's 16-byte chunk l ^ (j % 16), so that
+    //      the 16 rows of a read fall on different banks.  The staging areas
+    //      are the fp16 tile buffers (waves 0-2) and raw buffers 1 and 2
+    //      (wave 3), all free until the first tile is decoded.  The rope
+    //      parts (128 bytes a row) load directly.
+    const uint8_t* const q_stage = w < kNBuf ? &s_lc[w][0] : &s_raw[0][0] + kRawLcBytes;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int r = row0 + 32 * w + j;
+        const int64_t qrow = static_cast<int64_t>(b) * p.QH + (r < p.QH ? r : 0);
+        copy_to_lds_b128(reinterpret_cast<const uint8_t*>(p.q_lat + qrow * kKvLora),
+                         static_cast<uint32_t>(16 * (lane ^ (j & 15))), lds_addr(q_stage + 1024 * j));
+    }
     uint4 qv[36];
     {
         const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
-        const uint4* ql = reinterpret_cast<const uint4*>(p.q_lat + qrow * kKvLora);
         const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) qv[ks] = ql[2 * ks + g];
 #pragma unroll
         for (int r = 0; r < 4; ++r) qv[32 + r] = qr[4 * g + r];
     }
 
-    const int64_t L = p.kv_len[b];
-    const int64_t row_base = p.kv_start[b];
     int64_t ts, te;
     if (p.split_chunk > 0) {
         ts = static_cast<int64_t>(split) * p.split_chunk;
@@ -375,9 +413,11 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      layouts.  Copy k < 4 (Lc) takes token 2 w + lane / 32 + 8 k, whose
     //      chunk swizzle does not depend on k; copy 4 (i = 16, 17) takes Rc
     //      chunk 2 (i - 16) + lane / 32 of token lane % 32.
-    const int dma_tl = 2 * w + (lane >> 5);  // token of the wave's Lc copy 0
-    const int dma_lc = dma_tl * kRowBytes + 16 * ((lane & 31) ^ (8 * ((dma_tl >> 2) & 1)));
-    const int dma_rc = (lane & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (lane >> 5));
+    auto dma_tl = [&](int ln) { return 2 * w + (ln >> 5); };  // token of the wave's Lc copy 0
+    auto dma_lc = [&](int ln) {
+        return dma_tl(ln) * kRowBytes + 16 * ((ln & 31) ^ (8 * ((dma_tl(ln) >> 2) & 1)));
+    };
+    auto dma_rc = [&](int ln) { return (ln & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (ln >> 5)); };
     // The copies of a tile: tile i goes to raw Lc and scale buffer lbuf
     // (= i % 3) and raw Rc buffer i % 4.  Copy slot k < 4 of wave w is its Lc
     // copy k; slot 4 is the Rc copy of wave w (waves 0 and 1) or the tile's 32
@@ -386,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // by the last tile (a harmless re-copy into free buffers); tokens past
     // the range repeat its last row.  The per-lane byte offset is unsigned and
     // never negative.
-    auto issue_copy = [&](int tile, int lbuf, int k) {
+    auto issue_copy = [&](int tile, int lbuf, int k, int ln) {
         const int rbuf = tile & (kRcBufs - 1);  // (before the clamp)
         tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
@@ -395,30 +435,29 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         const bool full = te - t0 >= kTT;  // (uniform) fixed lane offsets
         const int valid = static_cast<int>(full ? kTT : te - t0);
         if (k < 4) {
-            const int past = full ? 0 : max(dma_tl + 8 * k - (valid - 1), 0);
-            copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc + (8 * k - past) * kRowBytes),
+            const int past = full ? 0 : max(dma_tl(ln) + 8 * k - (valid - 1), 0);
+            copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc(ln) + (8 * k - past) * kRowBytes),
                              lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
         } else if (w < 2) {
-            const int past = full ? 0 : max((lane & 31) - (valid - 1), 0);
-            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc - past * kRowBytes),
+            const int past = full ? 0 : max((ln & 31) - (valid - 1), 0);
+            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc(ln) - past * kRowBytes),
                              lds_addr(&s_rc[rbuf][1024 * w]));
         } else if (w == 3) {
-            const int tt = full ? (lane >> 1) : min(lane >> 1, valid - 1);
-            copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * (2 * tt + (lane & 1))),
+            const int tt = full ? (ln >> 1) : min(ln >> 1, valid - 1);
+            copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * (2 * tt + (ln & 1))),
                             lds_addr(&s_sc[lbuf][0]));
         }
     };
+    // (outside the tile loop, with offsets rebuilt from a fresh lane id)
     auto issue_tile = [&](int tile) {
+        const int ln = fresh_lane_id();
 #pragma unroll
-        for (int k = 0; k < 5; ++k) issue_copy(tile, tile % kNBuf, k);
+        for (int k = 0; k < 5; ++k) issue_copy(tile, tile % kNBuf, k, ln);
     };
 
-    // the first three tiles are in flight while the queries load
-    if (ntiles > 0) {
-        issue_tile(0);
-        issue_tile(1);
-        issue_tile(2);
-    }
+    // the first tile is in flight with the queries (tiles 1 and 2 go to
+    // buffers that stage the queries)
+    if (ntiles > 0) issue_tile(0);
 
     // ---- 2^e above the largest Lc scale of the token range
     uint32_t rbits = 0;
@@ -439,6 +478,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      Rc k-step r holds rope columns 32 g + 8 r .. +8 (the Rc operand
     //      below takes the same order).  Rows past Q*H (block padding) reuse
     //      row 0; their results are never stored.
+    wait_all_copies();  // (the queries, tile 0 and the scale loads)
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks)
+        qv[ks] = lds_load<uint4>(q_stage, 1024 * l32 + 16 * ((2 * ks + g) ^ (l32 & 15)));
     int kq = 0;
     {
         uint32_t mbits = 0;
@@ -451,13 +494,11 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 12;
             kq = kq < -100 ? -100 : (kq > 120 ? 120 : kq);
         }
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qv[ks] = bf16x8_to_f16(qv[ks], kq);
     }
 
     rbits = wave_max_u32(rbits);
     if (lane == 0) s_red[w] = rbits;
-    __syncthreads();
+    __syncthreads();  // (also: every wave has read its staged queries)
     rbits = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
     int e = 0;
     if (rbits != 0) {
@@ -465,6 +506,18 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         e = e < -126 ? -126 : e;
     }
     e = __builtin_amdgcn_readfirstlane(e);
+
+    // tiles 1 and 2 go to buffers that staged the queries; the conversion
+    // below (pinned after them) runs while they are in flight
+    if (ntiles > 0) {
+        issue_tile(1);
+        issue_tile(2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+        pin(qv[ks].x); pin(qv[ks].y); pin(qv[ks].z); pin(qv[ks].w);
+        qv[ks] = bf16x8_to_f16(qv[ks], kq);
+    }
 
     // ---- per-lane LDS offsets
     // score A operand, Lc k-step ks: token l32, chunk 2 ks + g
@@ -747,35 +800,42 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         else barrier_after_copies<5>();
     };
     for (int attempt = 0; attempt < 2; ++attempt) {
-        if (attempt > 0 && ntiles > 0) {
-            issue_tile(0);
-            issue_tile(1);
-            issue_tile(2);
-        }
         if (ntiles > 0) {
-            wait_vmcnt<0>();  // tiles 0, 1, 2
-            __syncthreads();
-#pragma unroll
-            for (int tile = 0; tile < 2; ++tile) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    decode_load(tile, j);
-                    decode_store(tile, j, 0);
-                    decode_store(tile, j, 1);
-                }
-                decode_scales(tile);
+            if (attempt > 0) {
+                issue_tile(0);
+                wait_all_copies();
+                __syncthreads();
+                issue_tile(1);
+                issue_tile(2);
             }
-            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                decode_load(0, j);
+                decode_store(0, j, 0);
+                decode_store(0, j, 1);
+            }
+            decode_scales(0);
+            end_barrier();  // tile 0 decoded; tile 1 landed, tile 2 may be in flight
             issue_tile(3);  // (raw buffers of tile 0, decoded)
             rope_load(0);
             score_begin(0);
-            static_for<36>([&](auto ks) { score_step(0, ks); });
+            static_for<36>([&](auto kc) {
+                constexpr int ks = decltype(kc)::value;
+                score_step(0, ks);
+                // decode of tile 1 between the score MFMAs (as in phase A)
+                if constexpr (ks >= 6 && ks <= 30 && (ks - 6) % 8 == 0) decode_load(1, (ks - 6) / 8);
+                if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(1, (ks - 9) / 8, 0);
+                if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(1, (ks - 11) / 8, 1);
+                if constexpr (ks == 35) decode_scales(1);
+            });
             mfma_acc_drain(accL, accR);
             static_for<kSoftSteps>([&](auto k) { soft_step(decltype(k)::value, 0, 0, true); });
             l_run += lsum;
             pa[0] = pn[0];
             pa[1] = pn[1];
-            end_barrier();  // tile 0's Rc codes are read before copy(4) reuses them
+            // tile 1 decoded, tile 2 landed; tile 0's Rc codes are read before
+            // copy(4) reuses them
+            end_barrier();
         }
         // iteration `it` with R = it % kNBuf known at compile time, so that
         // every LDS address is a lane offset plus an immediate
@@ -799,7 +859,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(B2, (ks - 9) / 8, 0);
                 if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(B2, (ks - 11) / 8, 1);
                 if constexpr (ks == 35) decode_scales(B2);
-                if constexpr (ks % 11 == 3) issue_copy(it + 4, B1, ks / 11);
+                if constexpr (ks % 11 == 3) issue_copy(it + 4, B1, ks / 11, lane);
                 order();
             });
             // ---------------- phase B: context(it) (it reads only buffers
@@ -812,7 +872,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 context_step(B0, n, n < 16 ? pa[0] : pa[1]);
                 if constexpr (n == 0) mfma_acc_drain(accL, accR);
                 if constexpr (n < kSoftSteps) soft_step(n, B1, it + 1, real_next);
-                if constexpr (n % 11 == 5 && n / 11 < 2) issue_copy(it + 4, B1, 3 + n / 11);
+                if constexpr (n % 11 == 5 && n / 11 < 2) issue_copy(it + 4, B1, 3 + n / 11, lane);
                 order();
             });
             l_run += real_next ? lsum : 0.0f;

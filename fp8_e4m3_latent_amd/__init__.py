@@ -199,7 +199,8 @@ def partials_bytes(B, Q, H, num_splits):
 def absorb_decode_partials(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len,
                            softmax_scale, split_tokens, num_splits, partials, stream=None):
     """Stage 1 of the decode: one partial softmax per token range into
-    `partials` (f32 GPU tensor of partials_bytes() bytes)."""
+    `partials` (a 1-D f32 GPU tensor used as raw storage, partials_bytes()
+    bytes: int16 codes of O, then f32 (m, l, o_scale, 0) per row)."""
     torch = _torch()
     args, _, _ = _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, False)
     pp = _check(partials, "partials", torch.float32, 1)

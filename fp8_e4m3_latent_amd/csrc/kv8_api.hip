@@ -166,9 +166,9 @@ int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
                                const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
                                int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
                                float softmax_scale, int32_t split_tokens, int32_t num_splits,
-                               float* partials, size_t partials_bytes, void* stream) {
+                               void* partials, size_t partials_bytes, void* stream) {
     int rc = check_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, B, Q, H,
-                          kv_lora, rope, softmax_scale, partials /* no out */);
+                          kv_lora, rope, softmax_scale, static_cast<float*>(partials) /* no out */);
     if (rc != KV8_OK) return rc;
     if (num_splits < 1 || num_splits > (1 << 20) || split_tokens < 0) return KV8_EINVAL;
     if (!partials || !aligned(partials, 256) ||
@@ -183,7 +183,7 @@ int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
     return launched(kv8::launch_absorb_decode(d, static_cast<hipStream_t>(stream), false));
 }
 
-int kv8_lse_merge(const float* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+int kv8_lse_merge(const void* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
                   int32_t num_splits, float softmax_scale, float* out, void* stream) {
     if (B < 1 || Q < 1 || H < 1 || num_splits < 1) return KV8_EINVAL;
     if (kv_lora != kv8::kKvLora) return KV8_EUNSUPPORTED;

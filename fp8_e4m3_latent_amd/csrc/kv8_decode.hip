@@ -99,8 +99,8 @@ struct DecodeArgs {
     int n_sub;         // split_chunk == 0: sub-ranges per equal range
     float c;           // softmax_scale * log2(e)
     float* out;        // [B][QH][512] when no partials are written
-    float* part_o;     // [n_splits][B][QH][512]
-    float* part_ml;    // [n_splits][B][QH][2]: reference score m, sum l
+    int16_t* part_o;   // [n_splits][B][QH][512] codes, O = code * o_scale
+    float* part_ml;    // [n_splits][B][QH][4]: reference score m, sum l, o_scale, 0
 };
 
 // s_waitcnt with only the vector-memory counter limited (lgkm and exp free)
@@ -904,34 +904,99 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                    "+a"(O[6]), "+a"(O[7]), "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]),
                    "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
     const float l_tot = pair_sum(l_run);
+    // (lane indices rebuilt here, so that no address of the stores below is
+    // computed before the tile loop and kept live across it)
+    const int el = fresh_lane_id();
+    const int e32 = el & 31, eg = el >> 5;
     if (p.part_o == nullptr) {
         // the probabilities carried 2^-e: out = 2^e O / l
-        if (g == 0) s_row[w][l32] = l_tot > 0.0f ? __builtin_ldexpf(1.0f / l_tot, e) : 0.0f;
-    } else {
-        if (g == 0 && row_ok) {
-            float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 2;
-            ml[0] = __builtin_ldexpf(sgn * m_x, kq);  // reference score in true units
-            ml[1] = l_tot;
-        }
-        if (g == 0) s_row[w][l32] = __builtin_ldexpf(1.0f, e);  // partial O in true units
-    }
-    __builtin_amdgcn_wave_barrier();
-    float* dst = p.part_o == nullptr
-                     ? p.out + static_cast<int64_t>(b) * p.QH * kKvLora
-                     : p.part_o + (static_cast<int64_t>(split) * p.B + b) * p.QH * kKvLora;
+        if (eg == 0) s_row[w][e32] = l_tot > 0.0f ? __builtin_ldexpf(1.0f / l_tot, e) : 0.0f;
+        __builtin_amdgcn_wave_barrier();
+        float* dst = p.out + static_cast<int64_t>(b) * p.QH * kKvLora;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 f4 = *reinterpret_cast<const float4*>(&s_row[w][8 * q4 + 4 * g]);
-        const float fv[4] = {f4.x, f4.y, f4.z, f4.w};
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 f4 = *reinterpret_cast<const float4*>(&s_row[w][8 * q4 + 4 * eg]);
+            const float fv[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int orow = row0 + 32 * w + 8 * q4 + 4 * g + r;
-            if (orow < p.QH) {
-                float* o = dst + static_cast<int64_t>(orow) * kKvLora + l32;
+            for (int r = 0; r < 4; ++r) {
+                const int orow = row0 + 32 * w + 8 * q4 + 4 * eg + r;
+                if (orow < p.QH) {
+                    float* o = dst + static_cast<int64_t>(orow) * kKvLora + e32;
 #pragma unroll
-                for (int dt = 0; dt < 16; ++dt) o[32 * dt] = O[dt][4 * q4 + r] * fv[r];
+                    for (int dt = 0; dt < 16; ++dt) {
+                        float v;
+                        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(O[dt][4 * q4 + r]));
+                        o[32 * dt] = v * fv[r];
+                    }
+                }
             }
         }
+        return;
+    }
+
+    // Partial O as 16-bit codes, one scale per row: code = round(32767 O /
+    // max_row |O|) (clamped to [-32767, 32767]), O = code * o_scale with
+    // o_scale = 2^e max_row |O| / 32767 in true units.  |O| is compared as
+    // the bit pattern of a non-negative float; the row maximum of register j
+    // (row 8 (j / 4) + 4 g + j % 4, columns 32 dt + l32) combines the 16
+    // registers of the lane and then the 32 lanes of its half.
+    // Rows j, j + 1 at a time: their 32 values are read once, their maxima
+    // reduced, and their codes stored.
+    auto row_max = [&](uint32_t m) {
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0xB1, 0xF, 0xF, false)));
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x4E, 0xF, 0xF, false)));
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x141, 0xF, 0xF, false)));
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x140, 0xF, 0xF, false)));
+        const auto sw = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+        return max(static_cast<uint32_t>(sw[0]), static_cast<uint32_t>(sw[1]));
+    };
+    int16_t* dst = p.part_o + (static_cast<int64_t>(split) * p.B + b) * p.QH * kKvLora;
+    uint32_t mine = 0;  // lane t < 16 of each half: the maximum of register t's row
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+        // (each pair of rows reads its 32 values from the AGPRs here)
+        float va[16], vb[16];
+        uint32_t ma = 0, mb = 0;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) {
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(va[dt]) : "a"(O[dt][j]));
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(vb[dt]) : "a"(O[dt][j + 1]));
+            ma = max(ma, __float_as_uint(va[dt]) & 0x7FFFFFFFu);
+            mb = max(mb, __float_as_uint(vb[dt]) & 0x7FFFFFFFu);
+        }
+        ma = row_max(ma);
+        mb = row_max(mb);
+        mine = (e32 & 15) == j ? ma : mine;
+        mine = (e32 & 15) == j + 1 ? mb : mine;
+        const float r0 = __uint_as_float(ma), r1 = __uint_as_float(mb);
+        // (an approximate reciprocal: only the code scale depends on it)
+        const float i0 = r0 > 0.0f ? __builtin_amdgcn_rcpf(r0) : 0.0f;
+        const float i1 = r1 > 0.0f ? __builtin_amdgcn_rcpf(r1) : 0.0f;
+        const int orow0 = row0 + 32 * w + 8 * (j >> 2) + 4 * eg + (j & 3);
+        int16_t* o0 = dst + static_cast<int64_t>(orow0) * kKvLora + e32;
+        int16_t* o1 = o0 + kKvLora;  // (row of register j + 1)
+        uint32_t c2[16];
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt)
+            c2[dt] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(va[dt] * i0, vb[dt] * i1));
+        if (orow0 < p.QH) {
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt) o0[32 * dt] = static_cast<int16_t>(c2[dt] & 0xFFFFu);
+        }
+        if (orow0 + 1 < p.QH) {
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt) o1[32 * dt] = static_cast<int16_t>(c2[dt] >> 16);
+        }
+        order();
+    }
+    if (e32 < 16) s_row[w][8 * (e32 >> 2) + 4 * eg + (e32 & 3)] = __uint_as_float(mine);
+    __builtin_amdgcn_wave_barrier();
+    if (eg == 0 && row_ok) {
+        float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 4;
+        const float rmax = s_row[w][e32];
+        *reinterpret_cast<float4*>(ml) =
+            make_float4(__builtin_ldexpf(sgn * m_x, kq),  // reference score in true units
+                        l_tot, __builtin_ldexpf(rmax * (1.0f / 32767.0f), e), 0.0f);
     }
 }
 
@@ -942,10 +1007,18 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 // Block = 256 threads = one (b, row) and one quarter (128 columns) of the
 // output row: 8 groups of 32 lanes, group g summing the splits s = g mod 8
 // (lane = 4 columns), then one reduction over the groups in LDS.
+// four 16-bit codes (two dwords, low half first) as floats
+__device__ __forceinline__ float4 codes4_to_f32(uint2 c) {
+    return make_float4(static_cast<float>(static_cast<int16_t>(c.x & 0xFFFFu)),
+                       static_cast<float>(static_cast<int16_t>(c.x >> 16)),
+                       static_cast<float>(static_cast<int16_t>(c.y & 0xFFFFu)),
+                       static_cast<float>(static_cast<int16_t>(c.y >> 16)));
+}
+
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = 8;
 constexpr int kMergeCols = kKvLora / 4;
-__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const int16_t* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml,
                                                                   int B, int QH, int n_splits, float c,
                                                                   float* __restrict__ out) {
@@ -961,7 +1034,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
     // m*: the largest (c > 0) or smallest (c < 0) reference with l > 0
     float mm = cpos ? -INFINITY : INFINITY;
     for (int s = tid; s < n_splits; s += kMergeThreads) {
-        const float2 ml = *reinterpret_cast<const float2*>(part_ml + (s * stride + br) * 2);
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + (s * stride + br) * 4);
         if (ml.y > 0.0f) mm = cpos ? fmaxf(mm, ml.x) : fminf(mm, ml.x);
     }
 #pragma unroll
@@ -980,40 +1053,44 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float lsum = 0.0f;
     if (any) {
-        const float* po = part_o + br * kKvLora + col0 + 4 * q;
+        const int16_t* po = part_o + br * kKvLora + col0 + 4 * q;
         int s = grp;
         // four splits in flight per lane
         for (; s + 3 * kMergeGroups < n_splits; s += 4 * kMergeGroups) {
-            float2 ml[4];
-            float4 o[4];
+            float4 ml[4];
+            uint2 o[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int64_t su = s + u * kMergeGroups;
-                ml[u] = *reinterpret_cast<const float2*>(part_ml + (su * stride + br) * 2);
-                o[u] = *reinterpret_cast<const float4*>(po + su * stride * kKvLora);
+                ml[u] = *reinterpret_cast<const float4*>(part_ml + (su * stride + br) * 4);
+                o[u] = *reinterpret_cast<const uint2*>(po + su * stride * kKvLora);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 if (ml[u].y > 0.0f) {
                     const float wgt = __builtin_amdgcn_exp2f(c * (ml[u].x - mm));
                     lsum += wgt * ml[u].y;
-                    acc.x += wgt * o[u].x;
-                    acc.y += wgt * o[u].y;
-                    acc.z += wgt * o[u].z;
-                    acc.w += wgt * o[u].w;
+                    const float4 v = codes4_to_f32(o[u]);
+                    const float ws = wgt * ml[u].z;
+                    acc.x += ws * v.x;
+                    acc.y += ws * v.y;
+                    acc.z += ws * v.z;
+                    acc.w += ws * v.w;
                 }
             }
         }
         for (; s < n_splits; s += kMergeGroups) {
-            const float2 ml = *reinterpret_cast<const float2*>(part_ml + (static_cast<int64_t>(s) * stride + br) * 2);
+            const float4 ml = *reinterpret_cast<const float4*>(part_ml + (static_cast<int64_t>(s) * stride + br) * 4);
             if (ml.y > 0.0f) {
-                const float4 o = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s) * stride * kKvLora);
+                const float4 v = codes4_to_f32(
+                    *reinterpret_cast<const uint2*>(po + static_cast<int64_t>(s) * stride * kKvLora));
                 const float wgt = __builtin_amdgcn_exp2f(c * (ml.x - mm));
                 lsum += wgt * ml.y;
-                acc.x += wgt * o.x;
-                acc.y += wgt * o.y;
-                acc.z += wgt * o.z;
-                acc.w += wgt * o.w;
+                const float ws = wgt * ml.z;
+                acc.x += ws * v.x;
+                acc.y += ws * v.y;
+                acc.z += ws * v.z;
+                acc.w += ws * v.w;
             }
         }
     }
@@ -1039,15 +1116,15 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
 // holding split s's (m, l), every lane summing 8 columns over the splits.
 constexpr int kMergeRowsPerBlock = 4;
 __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int B, int QH,
+    const int16_t* __restrict__ part_o, const float* __restrict__ part_ml, int B, int QH,
     int n_splits, float c, float* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int64_t br = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + (threadIdx.x >> 6);
     const int64_t stride = static_cast<int64_t>(B) * QH;
     if (br >= stride) return;
     const bool cpos = c >= 0.0f;
-    float2 ml = make_float2(0.0f, 0.0f);
-    if (lane < n_splits) ml = *reinterpret_cast<const float2*>(part_ml + (lane * stride + br) * 2);
+    float4 ml = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (lane < n_splits) ml = *reinterpret_cast<const float4*>(part_ml + (lane * stride + br) * 4);
     float mm = ml.y > 0.0f ? ml.x : (cpos ? -INFINITY : INFINITY);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -1058,24 +1135,26 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel
     float lsum = wgt * ml.y;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+    const float wsc = wgt * ml.z;  // weight of split `lane`'s codes
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-    const float* po = part_o + br * kKvLora + 4 * lane;
+    const int16_t* po = part_o + br * kKvLora + 8 * lane;
     for (int s2 = 0; s2 < n_splits; ++s2) {
-        const float w2 = __shfl(wgt, s2, 64);
-        if (w2 > 0.0f) {  // (uniform)
-            const float4 o0 = *reinterpret_cast<const float4*>(po + s2 * stride * kKvLora);
-            const float4 o1 = *reinterpret_cast<const float4*>(po + s2 * stride * kKvLora + 256);
-            a0.x += w2 * o0.x; a0.y += w2 * o0.y; a0.z += w2 * o0.z; a0.w += w2 * o0.w;
-            a1.x += w2 * o1.x; a1.y += w2 * o1.y; a1.z += w2 * o1.z; a1.w += w2 * o1.w;
+        const float w2 = __shfl(wsc, s2, 64);
+        if (w2 != 0.0f) {  // (uniform)
+            const uint4 o8 = *reinterpret_cast<const uint4*>(po + s2 * stride * kKvLora);
+            const float4 v0 = codes4_to_f32(make_uint2(o8.x, o8.y));
+            const float4 v1 = codes4_to_f32(make_uint2(o8.z, o8.w));
+            a0.x += w2 * v0.x; a0.y += w2 * v0.y; a0.z += w2 * v0.z; a0.w += w2 * v0.w;
+            a1.x += w2 * v1.x; a1.y += w2 * v1.y; a1.z += w2 * v1.z; a1.w += w2 * v1.w;
         }
     }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    float* o = out + br * kKvLora + 4 * lane;
+    float* o = out + br * kKvLora + 8 * lane;
     *reinterpret_cast<float4*>(o) = make_float4(a0.x * inv, a0.y * inv, a0.z * inv, a0.w * inv);
-    *reinterpret_cast<float4*>(o + 256) = make_float4(a1.x * inv, a1.y * inv, a1.z * inv, a1.w * inv);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(a1.x * inv, a1.y * inv, a1.z * inv, a1.w * inv);
 }
 
-void launch_merge(const float* part_o, const float* part_ml, int B, int QH, int n_splits, float c,
+void launch_merge(const int16_t* part_o, const float* part_ml, int B, int QH, int n_splits, float c,
                   float* out, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(B) * QH;
     if (n_splits <= 64) {
@@ -1092,7 +1171,7 @@ void launch_merge(const float* part_o, const float* part_ml, int B, int QH, int 
 
 size_t splitT_workspace_bytes(int B, int Q, int H, int n_splits) {
     const size_t rows = static_cast<size_t>(n_splits) * B * Q * H;
-    return rows * kKvLora * sizeof(float) + rows * 2 * sizeof(float);
+    return rows * kKvLora * sizeof(int16_t) + rows * 4 * sizeof(float);
 }
 
 int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) {
@@ -1117,8 +1196,8 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) 
     a.part_ml = nullptr;
     if (d.n_splits > 1 || !merge) {
         const size_t rows = static_cast<size_t>(d.n_splits) * d.B * a.QH;
-        a.part_o = static_cast<float*>(d.workspace);
-        a.part_ml = a.part_o + rows * kKvLora;
+        a.part_o = static_cast<int16_t*>(d.workspace);
+        a.part_ml = reinterpret_cast<float*>(a.part_o + rows * kKvLora);
     }
     const int64_t blocks = static_cast<int64_t>(d.B) * a.n_splits * a.n_rb;
     hipLaunchKernelGGL(absorb_decode_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
@@ -1131,11 +1210,12 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) 
     return 0;
 }
 
-int launch_lse_merge(const float* partials, int B, int QH, int n_splits, float softmax_scale,
+int launch_lse_merge(const void* partials, int B, int QH, int n_splits, float softmax_scale,
                      float* out, hipStream_t stream) {
     const size_t rows = static_cast<size_t>(n_splits) * B * QH;
-    const float* ml = partials + rows * kKvLora;
-    launch_merge(partials, ml, B, QH, n_splits, softmax_scale * 1.4426950408889634f, out, stream);
+    const int16_t* po = static_cast<const int16_t*>(partials);
+    const float* ml = reinterpret_cast<const float*>(po + rows * kKvLora);
+    launch_merge(po, ml, B, QH, n_splits, softmax_scale * 1.4426950408889634f, out, stream);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -38,7 +38,7 @@ struct DecodeLaunch {
 size_t splitT_workspace_bytes(int B, int Q, int H, int n_splits);
 // decode kernel (+ merge when n_splits > 1 and `merge` is set)
 int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge = true);
-int launch_lse_merge(const float* partials, int B, int QH, int n_splits, float softmax_scale,
+int launch_lse_merge(const void* partials, int B, int QH, int n_splits, float softmax_scale,
                      float* out, hipStream_t stream);
 
 int launch_decode_codes(const uint8_t* codes, int64_t n, uint16_t* bf, uint16_t* hf,

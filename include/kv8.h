@@ -143,11 +143,17 @@ int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope,
  * stage 2 merges the partials by log-sum-exp.  Partials of several devices
  * holding different token ranges of one sequence can be merged the same way.
  *
- * Partials buffer (device, f32, caller-owned, 256-byte aligned), R = Q*H:
- *   O  [num_splits][B][R][kv_lora]  sum_t 2^(c (x_t - m)) scale_Lc[t] dec(Lc_t)
- *   ml [num_splits][B][R][2]        m = reference score, l = sum_t 2^(c (x_t - m))
- * with x_t = q_lat . xhat_Lc[t] + q_rope . xhat_Rc[t] (before softmax_scale),
- * c = softmax_scale * log2(e); a range with no visible row has l = 0. */
+ * Partials buffer (device, caller-owned, 256-byte aligned), R = Q*H:
+ *   O  int16 [num_splits][B][R][kv_lora]  codes of
+ *                                         sum_t 2^(c (x_t - m)) scale_Lc[t] dec(Lc_t)
+ *   ml f32   [num_splits][B][R][4]        m = reference score,
+ *                                         l = sum_t 2^(c (x_t - m)), o_scale, 0
+ * (ml follows O directly).  O of a row is code * o_scale, with the codes
+ * rounded from 32767 O / max |O| over the row (max |O| = 32767 o_scale; a
+ * row with O = 0 has o_scale = 0): 16 bits per value with an absolute error
+ * of at most max |O| / 65534 on each.  With x_t = q_lat . xhat_Lc[t] +
+ * q_rope . xhat_Rc[t] (before softmax_scale), c = softmax_scale * log2(e);
+ * a range with no visible row has l = 0. */
 
 /* Bytes of a partials buffer for these shapes. */
 size_t kv8_partials_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t num_splits);
@@ -165,13 +171,13 @@ int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
                                const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
                                int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
                                float softmax_scale, int32_t split_tokens, int32_t num_splits,
-                               float* partials, size_t partials_bytes, void* stream);
+                               void* partials, size_t partials_bytes, void* stream);
 
 /* Stage 2 ([colibri#299] PR description, follow-up: split-T kernels):
  * out[b][r] = sum_s w_s O_s / sum_s w_s l_s over ranges with l_s > 0,
  * w_s = 2^(c (m_s - m*)), m* the reference with the largest c m_s; zero when
  * no range saw a row. */
-int kv8_lse_merge(const float* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+int kv8_lse_merge(const void* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
                   int32_t num_splits, float softmax_scale, float* out, void* stream);
 
 /* Human-readable name of a kv8_status value (static string, never NULL). */

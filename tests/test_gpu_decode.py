@@ -247,7 +247,7 @@ def test_partials_of_two_shards_merge(kv8):
         kv8.absorb_decode_partials(ql, qr, codes, scales, s0, l0, w.max_len, w.softmax_scale,
                                    0, 1, p)
         parts.append(p)
-    n_o = w.B * R * KL
+    n_o = w.B * R * KL // 2  # (int16 codes of O, in f32 units of the buffer)
     merged = torch.cat([parts[0][:n_o], parts[1][:n_o], parts[0][n_o:], parts[1][n_o:]])
     out = kv8.lse_merge(merged, w.B, w.Q, w.H, 2, w.softmax_scale)
     torch.cuda.synchronize()

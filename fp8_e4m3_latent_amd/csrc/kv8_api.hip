@@ -87,7 +87,9 @@ int check_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* c
         !aligned(scales, 8) || !aligned(kv_start, 8) || !aligned(kv_len, 4) || !aligned(out, 16))
         return KV8_EINVAL;
     const int64_t blocks = static_cast<int64_t>(B) * row_blocks(Q, H);
-    if (blocks > (int64_t(1) << 30) || static_cast<int64_t>(Q) * H > (int64_t(1) << 24))
+    // (a sequence's latent query rows must span less than 2^31 bytes: the
+    // decode addresses them with 32-bit offsets)
+    if (blocks > (int64_t(1) << 30) || static_cast<int64_t>(Q) * H > (int64_t(1) << 21))
         return KV8_EUNSUPPORTED;
     return KV8_OK;
 }

@@ -271,13 +271,17 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Packed maximum of the magnitudes of two bf16 pairs: the bit patterns of
+// non-negative bf16 values order as unsigned 16-bit integers.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t absmax2_bf16x2(uint32_t m, uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, m),
+                                                                  __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu)));
+}
+
 // bf16 bits -> f32
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) {
-    return max((w << 16) & 0x7FFFFFFFu, w & 0x7FFF0000u);
-}
 
 // 8 bf16 values times 2^-k -> 8 fp16 values (exact for the scaled range)
 __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 q, int k) {
@@ -363,12 +367,17 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      (wave 3), all free until the first tile is decoded.  The rope
     //      parts (128 bytes a row) load directly.
     const uint8_t* const q_stage = w < kNBuf ? &s_lc[w][0] : &s_raw[0][0] + kRawLcBytes;
+    {
+        // (offsets from the sequence's first row: below 2^31, Q*H <= 2^21)
+        const uint8_t* q_seq = reinterpret_cast<const uint8_t*>(p.q_lat + static_cast<int64_t>(b) * p.QH * kKvLora);
+        const uint32_t lds0 = lds_addr(q_stage);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const int r = row0 + 32 * w + j;
-        const int64_t qrow = static_cast<int64_t>(b) * p.QH + (r < p.QH ? r : 0);
-        copy_to_lds_b128(reinterpret_cast<const uint8_t*>(p.q_lat + qrow * kKvLora),
-                         static_cast<uint32_t>(16 * (lane ^ (j & 15))), lds_addr(q_stage + 1024 * j));
+        for (int j = 0; j < 32; ++j) {
+            const int r = row0 + 32 * w + j;
+            const int rr = r < p.QH ? r : 0;  // (uniform)
+            copy_to_lds_b128(q_seq, static_cast<uint32_t>(1024 * rr + 16 * (lane ^ (j & 15))),
+                             lds0 + 1024 * j);
+        }
     }
     uint4 qv[36];
     {
@@ -484,11 +493,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         qv[ks] = lds_load<uint4>(q_stage, 1024 * l32 + 16 * ((2 * ks + g) ^ (l32 & 15)));
     int kq = 0;
     {
-        uint32_t mbits = 0;
+        uint32_t m2 = 0;
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks)
-            mbits = max(max(mbits, max(absmax_bf16x2(qv[ks].x), absmax_bf16x2(qv[ks].y))),
-                        max(absmax_bf16x2(qv[ks].z), absmax_bf16x2(qv[ks].w)));
+            m2 = absmax2_bf16x2(absmax2_bf16x2(absmax2_bf16x2(absmax2_bf16x2(m2, qv[ks].x), qv[ks].y),
+                                               qv[ks].z), qv[ks].w);
+        const uint32_t mbits = max(m2 << 16, m2 & 0xFFFF0000u);  // (f32 bits)
         const float qmax = fmaxf(__uint_as_float(mbits), other_half(__uint_as_float(mbits)));
         if (qmax > 0.0f) {
             kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 12;

@@ -39,8 +39,8 @@
  *     and nothing is launched; data is never an error (NaN, inf, zero and
  *     subnormal values have defined results); nothing aborts or prints.
  *
- * Supported shapes: kv_lora = 512, rope = 64 (other values return
- * KV8_EUNSUPPORTED).
+ * Supported shapes: kv_lora = 512, rope = 64, Q*H <= 2^21 query rows per
+ * sequence (other values return KV8_EUNSUPPORTED).
  */
 #ifndef KV8_H
 #define KV8_H

@@ -14,7 +14,9 @@ latent rows of 512 Lc + 64 Rc e4m3 codes with per-row f32 scales.  Each step
 Three copies of the cache (3 x 153 MB, more than the 256 MB last-level cache)
 are used in rotation so every step reads its KV from HBM.  Inputs are resident
 in HBM before the timed region; times come from HIP events on the stream the
-kernels run on.  The decode kernel's roofline uses its duration over launches
+kernels run on.  The default 400 untimed steps (about 50 ms) bring the GPU to
+its working clock first: with a handful of warmup steps the timed steps ran
+about 15% slower.  The decode kernel's roofline uses its duration over launches
 of that kernel alone, back to back on the same rotating caches (the per-step
 events around it also hold its dispatch gap behind the append kernel).
 
@@ -294,8 +296,8 @@ def roofline_hbm(nbytes, ms, traffic):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--legs", default="decode,quantize,splitT",
                     help="comma list of decode, quantize, splitT, ragged, copy")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096,

@@ -169,6 +169,34 @@ __device__ __forceinline__ void copy_to_lds_b32(const void* base, uint32_t off, 
                  : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
+// The same copies through a raw buffer resource (base, no stride,
+// num_records = nbytes): the buffer range check turns every dword of a lane
+// at or past base + nbytes into a zero written to LDS, without a memory
+// access.  Word 3 holds the raw-buffer format bits of this architecture.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t nbytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = static_cast<int>(static_cast<uint32_t>(a));
+    r.y = static_cast<int>(static_cast<uint32_t>(a >> 32));  // (stride 0)
+    r.z = static_cast<int>(nbytes);
+    r.w = 0x00020000;
+    return r;
+}
+__device__ __forceinline__ void copy_to_lds_b128_rc(const void* base, uint32_t nbytes, uint32_t off,
+                                                    uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(buffer_rsrc(base, nbytes)), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void copy_to_lds_b32_rc(const void* base, uint32_t nbytes, uint32_t off,
+                                                   uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(buffer_rsrc(base, nbytes)), "s"(lds)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)p));
 }
@@ -432,29 +460,28 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // copy k; slot 4 is the Rc copy of wave w (waves 0 and 1) or the tile's 32
     // (Lc, Rc) scale pairs, 4 bytes per lane (wave 3): waves 0, 1 and 3 issue
     // five copies per tile, wave 2 four.  Tiles past the range are replaced
-    // by the last tile (a harmless re-copy into free buffers); tokens past
-    // the range repeat its last row.  The per-lane byte offset is unsigned and
-    // never negative.
+    // by the last tile (a harmless re-copy into free buffers).  The copies
+    // are range-checked at the range's end: rows past it arrive as zero codes
+    // and zero scales (masked tokens, whose weight is 0).  The per-lane byte
+    // offsets do not depend on the tile; copy k's first row (8 k) goes into
+    // the base.
     auto issue_copy = [&](int tile, int lbuf, int k, int ln) {
         const int rbuf = tile & (kRcBufs - 1);  // (before the clamp)
         tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
-        const float* sbase = p.scales + 2 * (row_base + t0);
-        const bool full = te - t0 >= kTT;  // (uniform) fixed lane offsets
-        const int valid = static_cast<int>(full ? kTT : te - t0);
+        const int valid = static_cast<int>(te - t0 < kTT ? te - t0 : kTT);  // (uniform, >= 1)
         if (k < 4) {
-            const int past = full ? 0 : max(dma_tl(ln) + 8 * k - (valid - 1), 0);
-            copy_to_lds_b128(base, static_cast<uint32_t>(dma_lc(ln) + (8 * k - past) * kRowBytes),
-                             lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
+            const int rows = valid - 8 * k > 0 ? valid - 8 * k : 0;
+            copy_to_lds_b128_rc(base + 8 * k * kRowBytes, static_cast<uint32_t>(rows * kRowBytes),
+                                static_cast<uint32_t>(dma_lc(ln)),
+                                lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
         } else if (w < 2) {
-            const int past = full ? 0 : max((ln & 31) - (valid - 1), 0);
-            copy_to_lds_b128(base, static_cast<uint32_t>(dma_rc(ln) - past * kRowBytes),
-                             lds_addr(&s_rc[rbuf][1024 * w]));
+            copy_to_lds_b128_rc(base, static_cast<uint32_t>(valid * kRowBytes),
+                                static_cast<uint32_t>(dma_rc(ln)), lds_addr(&s_rc[rbuf][1024 * w]));
         } else if (w == 3) {
-            const int tt = full ? (ln >> 1) : min(ln >> 1, valid - 1);
-            copy_to_lds_b32(sbase, static_cast<uint32_t>(4 * (2 * tt + (ln & 1))),
-                            lds_addr(&s_sc[lbuf][0]));
+            copy_to_lds_b32_rc(p.scales + 2 * (row_base + t0), static_cast<uint32_t>(8 * valid),
+                               static_cast<uint32_t>(4 * ln), lds_addr(&s_sc[lbuf][0]));
         }
     };
     // (outside the tile loop, with offsets rebuilt from a fresh lane id)

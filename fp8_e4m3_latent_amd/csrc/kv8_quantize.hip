@@ -80,13 +80,18 @@ __device__ __forceinline__ uint32_t encode4(float4 v, float inv, bool finite) {
 }
 
 constexpr int kQuantWaves = 4;    // waves per 256-thread block
-constexpr int kRowsPerWave = 8;
-constexpr int kSegs = 2 * kRowsPerWave;  // (row, Lc/Rc) segments of a wave
+constexpr int64_t kFewRows = 8192;  // below: one row per wave
 
+// kRowsPerWave rows per wave: 8 for bulk work (eight rows of loads in flight
+// per wave), 1 for a few rows (the per-token append of a decode step, where
+// the kernel's latency is what counts: one row per wave spreads the rows
+// over more compute units and shortens each wave's chain).
+template <int kRowsPerWave>
 __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     const float* __restrict__ src, int64_t stride, int64_t n_rows,
     uint8_t* __restrict__ codes, float* __restrict__ scales,
     const int64_t* __restrict__ dst_rows) {
+    constexpr int kSegs = 2 * kRowsPerWave;  // (row, Lc/Rc) segments of a wave
     const int lane = threadIdx.x & 63;
     const int64_t row0 =
         (static_cast<int64_t>(blockIdx.x) * kQuantWaves + (threadIdx.x >> 6)) * kRowsPerWave;
@@ -207,11 +212,18 @@ __global__ __launch_bounds__(256) void decode_codes_kernel(const uint8_t* __rest
 
 int launch_quantize_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
                          float* scales, const int64_t* dst_rows, hipStream_t stream) {
-    const int64_t rows_per_block = static_cast<int64_t>(kQuantWaves) * kRowsPerWave;
-    const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL(quantize_rows_kernel, dim3(static_cast<uint32_t>(blocks)),
-                       dim3(64 * kQuantWaves), 0, stream, src, stride, n_rows, codes, scales,
-                       dst_rows);
+    if (n_rows < kFewRows) {
+        const int64_t blocks = (n_rows + kQuantWaves - 1) / kQuantWaves;
+        hipLaunchKernelGGL(quantize_rows_kernel<1>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(64 * kQuantWaves), 0, stream, src, stride, n_rows, codes, scales,
+                           dst_rows);
+    } else {
+        const int64_t rows_per_block = static_cast<int64_t>(kQuantWaves) * 8;
+        const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+        hipLaunchKernelGGL(quantize_rows_kernel<8>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(64 * kQuantWaves), 0, stream, src, stride, n_rows, codes, scales,
+                           dst_rows);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

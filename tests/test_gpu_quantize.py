@@ -145,6 +145,12 @@ def test_quantize_deterministic_and_guard_band(kv8):
     rc, rs = oracle.quantize_rows(rows)
     assert_same(*a, rc, rs, "guard")
     assert_same(*b, rc, rs, "guard (second run)")
+    # the same rows in a batch of 8,320 (the many-rows launch shape; the 64
+    # above use the few-rows one)
+    say("quantize: guard band and special rows in a batch of 8320")
+    big = np.tile(rows, (130, 1))
+    c2, s2 = quantize_on_gpu(kv8, big)
+    assert_same(c2, s2, np.tile(rc, (130, 1)), np.tile(rs, (130, 1)), "guard (8320 rows)")
 
 
 def test_quantize_argument_errors(kv8):

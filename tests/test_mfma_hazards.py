@@ -12,6 +12,10 @@ This test compiles the kernel for gfx950 and checks the generated code:
 
 Wait states are counted as one per instruction and N + 1 per s_nop N; a
 label inside the window ends the search (the kernel places none there).
+
+It also checks that the innermost loop of the kernel (the tile loop) holds
+no scratch (spill) access: a reload there waits for every tile copy in
+flight, which stalls the copy pipeline.
 """
 import os
 import re
@@ -66,7 +70,7 @@ def _defs_uses(op, ops):
 
 
 @pytest.fixture(scope="module")
-def asm_lines(tmp_path_factory):
+def asm_text(tmp_path_factory):
     try:
         hipcc = build.hipcc()
     except RuntimeError:
@@ -76,7 +80,12 @@ def asm_lines(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("asm") / "kv8_decode.s")
     subprocess.run([hipcc, *build.flags(), "--cuda-device-only", "-S", SRC, "-o", out],
                    check=True, capture_output=True)
-    ins = [x for x in (_parse(l) for l in open(out)) if x]
+    return open(out).read().split("\n")
+
+
+@pytest.fixture(scope="module")
+def asm_lines(asm_text):
+    ins = [x for x in (_parse(l) for l in asm_text) if x]
     assert sum(1 for op, _ in ins if op.startswith("v_mfma")) > 0
     return ins
 
@@ -126,4 +135,36 @@ def test_mfma_vgpr_results_are_not_touched_before_their_latency(asm_lines):
                     bad.append((i, "%s %s" % (pop, ",".join(pops))))
             ws += _wait_states(pop, pops)
             j += 1
+    assert not bad, bad[:5]
+
+
+def test_no_scratch_access_in_the_tile_loop(asm_text):
+    # the decode kernel's loops: labels the compiler annotates with their
+    # depth; the tile loop is the one at depth 2 (inside the restart pass)
+    kern = "absorb_decode_kernel"
+    start = next(i for i, l in enumerate(asm_text)
+                 if kern in l and l.split(";")[0].rstrip().endswith(":"))
+    end = next(i for i in range(start, len(asm_text)) if asm_text[i].strip() == "s_endpgm")
+    body = asm_text[start:end]
+    # the loop header's label line, and then a comment naming it a depth-2
+    # loop header (on the same line or the next)
+    header = None
+    for i, l in enumerate(body):
+        if "Loop Header: Depth=2" in l:
+            k = i
+            while not re.match(r"^\.LBB\d+_\d+:", body[k]):
+                k -= 1
+            header = body[k].split(":")[0][1:]
+            break
+    assert header, "no depth-2 loop found"
+    first = next(i for i, l in enumerate(body) if l.startswith("." + header + ":"))
+    last = max(i for i, l in enumerate(body) if ("Header=" + header[1:]) in l or
+               l.startswith("." + header + ":"))
+    # through the loop's backward branch
+    j = last
+    while "s_cbranch" not in body[j] and "s_branch" not in body[j]:
+        j += 1
+    loop = body[first:j + 1]
+    assert sum(1 for l in loop if "v_mfma" in l) >= 68, "tile loop not found"
+    bad = [l.strip() for l in loop if "scratch_" in l]
     assert not bad, bad[:5]

@@ -255,3 +255,54 @@ def test_partials_of_two_shards_merge(kv8):
                            softmax_scale=w.softmax_scale)
     e = rel_err(out.cpu().numpy().reshape(-1, KL), ref.reshape(-1, KL))
     assert e <= TOL, e
+
+
+def test_step_graph_replay_matches_eager(kv8):
+    """A decode step (append of one fresh row per sequence, split partials,
+    merge) captured in a HIP graph and replayed three times, with eager steps
+    and synchronisations between the replays, reproduces the eager step bit
+    for bit on every replay; the eager step itself matches the oracle on the
+    appended cache."""
+    w = workloads.tiny(seed=23, B=4, Q=1, H=128, T=3000, outlier_p=0.0)
+    codes, scales, _, _ = build_cache(kv8, w.rows)
+    ql, qr, st, ln = to_dev(w)
+    fresh_h = workloads.fresh_rows(24, w.B)
+    fresh = torch.from_numpy(fresh_h).cuda()
+    dst = st + (ln.to(torch.int64) - 1)
+    k, n = kv8.decode_plan(w.B, w.Q, w.H, w.max_len)
+    part = torch.empty(kv8.partials_bytes(w.B, w.Q, w.H, n) // 4, dtype=torch.float32,
+                       device="cuda")
+    out = torch.empty((w.B, w.Q, w.H, KL), dtype=torch.float32, device="cuda")
+
+    def step():
+        kv8.quantize_rows(fresh, codes, scales, dst_rows=dst)
+        kv8.absorb_decode_partials(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale,
+                                   k, n, part)
+        kv8.lse_merge(part, w.B, w.Q, w.H, n, w.softmax_scale, out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    o = oracle.attention(w.q_lat, w.q_rope, c, s, w.kv_start, w.kv_len, Q=w.Q,
+                         softmax_scale=w.softmax_scale)
+    assert rel_err(ref.cpu().numpy().reshape(-1, KL), o.reshape(-1, KL)) <= TOL
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        step()                      # eager work between the replays
+        torch.cuda.synchronize()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("graph replay %d" % r)
+        assert torch.equal(out, ref), "replay %d differs from the eager step" % r

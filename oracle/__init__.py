@@ -53,6 +53,10 @@ def lib():
     L.orc_attention.argtypes = att + [_u8p, _f32p] + tail
     L.orc_attention_f32rows.restype = ctypes.c_int
     L.orc_attention_f32rows.argtypes = att + [_f32p, ctypes.c_int64] + tail
+    L.orc_norm_rope_rows.restype = None
+    L.orc_norm_rope_rows.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.c_int32, _f32p, ctypes.c_float, _i64p, ctypes.c_float,
+                                     _f32p, ctypes.c_int]
     L.orc_bytes_per_token_layer.restype = ctypes.c_int64
     L.orc_bytes_per_token_layer.argtypes = [ctypes.c_int32, ctypes.c_int32]
     _lib = L
@@ -125,6 +129,23 @@ def quantize_rows(src, kv_lora=512, rope=64, dst_rows=None, n_cache_rows=None,
     lib().orc_quantize_rows(_p(a, _f32p), a.strides[0] // 4, n, kv_lora, rope,
                             _p(codes, _u8p), _p(scales, _f32p), dp, _t(threads))
     return codes, scales
+
+
+def norm_rope_rows(src, norm_weight, eps, positions, rope_theta, kv_lora=512, rope=64,
+                   threads=0):
+    """The producer step: RMS-normalised Lc and rotary-embedded Rc of f32 rows
+    [n, >= kv_lora+rope], computed in f64 and rounded to f32 -> [n, kv_lora+rope]."""
+    a = np.asarray(src, dtype=np.float32)
+    assert a.ndim == 2 and a.strides[1] == 4
+    n = a.shape[0]
+    w = np.ascontiguousarray(norm_weight, dtype=np.float32)
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    assert w.size == kv_lora and pos.size == n
+    out = np.empty((n, kv_lora + rope), dtype=np.float32)
+    lib().orc_norm_rope_rows(_p(a, _f32p), a.strides[0] // 4, n, kv_lora, rope, _p(w, _f32p),
+                             float(eps), _p(pos, _i64p), float(rope_theta), _p(out, _f32p),
+                             _t(threads))
+    return out
 
 
 def _attn_common(q_lat, q_rope, kv_start, kv_len, Q, sel):

@@ -330,6 +330,40 @@ int orc_attention_f32rows(const uint16_t* q_lat, const uint16_t* q_rope,
     return 0;
 }
 
+// [colibri#299] commit message, attention_rows item: the fresh row is
+// normalised (Lc) and rotary-embedded (Rc) before it is quantized.  The
+// forms follow the standard definitions stated in kv8_oracle.h: RMS
+// normalisation with a weight, and rotation of interleaved pairs by position
+// times a geometric frequency.
+void orc_norm_rope_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
+                        int32_t kv_lora, int32_t rope, const float* norm_weight, float eps,
+                        const int64_t* positions, float rope_theta, float* out, int threads) {
+    const int64_t d = static_cast<int64_t>(kv_lora) + rope;
+    std::vector<float> freq(static_cast<size_t>(rope / 2));
+    for (int32_t i = 0; i < rope / 2; ++i)
+        freq[static_cast<size_t>(i)] = static_cast<float>(
+            std::pow(static_cast<double>(rope_theta), -2.0 * i / static_cast<double>(rope)));
+    parallel_for(n_rows, threads, [&](int64_t r) {
+        const float* x = src + r * src_row_stride;
+        float* y = out + r * d;
+        // Lc: y_j = w_j x_j / sqrt(mean x^2 + eps)
+        double ss = 0.0;
+        for (int32_t j = 0; j < kv_lora; ++j) ss += static_cast<double>(x[j]) * x[j];
+        const double rms = std::sqrt(ss / kv_lora + static_cast<double>(eps));
+        for (int32_t j = 0; j < kv_lora; ++j)
+            y[j] = static_cast<float>(static_cast<double>(norm_weight[j]) * x[j] / rms);
+        // Rc: pair (2i, 2i+1) rotated by a_i = fl32(fl32(pos) f_i)
+        const float pos = static_cast<float>(positions[r]);
+        for (int32_t i = 0; i < rope / 2; ++i) {
+            const float a = pos * freq[static_cast<size_t>(i)];
+            const double c = std::cos(static_cast<double>(a)), s = std::sin(static_cast<double>(a));
+            const double x0 = x[kv_lora + 2 * i], x1 = x[kv_lora + 2 * i + 1];
+            y[kv_lora + 2 * i] = static_cast<float>(x0 * c - x1 * s);
+            y[kv_lora + 2 * i + 1] = static_cast<float>(x0 * s + x1 * c);
+        }
+    });
+}
+
 int64_t orc_bytes_per_token_layer(int32_t kv_lora, int32_t rope) {
     return static_cast<int64_t>(kv_lora) + rope + 2 * static_cast<int64_t>(sizeof(float));
 }

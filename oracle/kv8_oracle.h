@@ -76,6 +76,22 @@ int orc_attention_f32rows(const uint16_t* q_lat, const uint16_t* q_rope,
                           float softmax_scale, int32_t num_splits,
                           const int64_t* sel, int64_t n_sel, double* out, int threads);
 
+/* The producer step in front of the quantizer ([colibri#299] commit message,
+ * attention_rows item: the producer quantizes the fresh normalised and
+ * rotary-embedded latent row).  The page names both steps but not their form;
+ * this takes the standard ones, computed in f64 and rounded to f32 once:
+ *   Lc (kv_lora values): RMS normalisation with a per-channel weight,
+ *     y_j = w_j x_j / sqrt(mean_k x_k^2 + eps);
+ *   Rc (rope values, even): rotary embedding of the interleaved pairs
+ *     (2i, 2i+1), i < rope/2, by the angle a_i = fl32(fl32(pos) f_i) with the
+ *     f32 frequency f_i = fl32(theta^(-2i/rope)):
+ *     y_2i = x_2i cos a_i - x_2i+1 sin a_i,  y_2i+1 = x_2i sin a_i + x_2i+1 cos a_i.
+ * src rows have stride src_row_stride floats; out is [n_rows][kv_lora+rope]
+ * f32.  The row then goes to orc_quantize_rows unchanged. */
+void orc_norm_rope_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
+                        int32_t kv_lora, int32_t rope, const float* norm_weight, float eps,
+                        const int64_t* positions, float rope_theta, float* out, int threads);
+
 /* Bytes one token occupies per layer: kv_lora + rope code bytes plus the two
  * f32 scales ([colibri#299] PR description: one f32 scale each for Lc, Rc). */
 int64_t orc_bytes_per_token_layer(int32_t kv_lora, int32_t rope);

@@ -24,7 +24,7 @@ _STATUS = {0: "KV8_OK", -1: "KV8_EINVAL", -2: "KV8_EUNSUPPORTED", -3: "KV8_ELAUN
            -4: "KV8_EWORKSPACE", -5: "KV8_ENOMEM"}
 
 # every symbol include/kv8.h declares
-EXPORTS = ("kv8_quantize_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
+EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
            "kv8_absorb_decode_splitT", "kv8_partials_bytes", "kv8_decode_plan",
            "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
            "kv8_encode_bits", "kv8_decode_codes")
@@ -54,6 +54,9 @@ def lib():
     L.kv8_status_string.argtypes = [ctypes.c_int]
     L.kv8_quantize_rows.restype = ctypes.c_int
     L.kv8_quantize_rows.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+    L.kv8_norm_rope_quantize_rows.restype = ctypes.c_int
+    L.kv8_norm_rope_quantize_rows.argtypes = [vp, i64, i64, i32, i32, vp, f32, vp, f32, vp, vp,
+                                              vp, vp]
     dec = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
     L.kv8_absorb_decode.restype = ctypes.c_int
     L.kv8_absorb_decode.argtypes = dec + [vp]
@@ -131,6 +134,40 @@ def quantize_rows(src, codes, scales, dst_rows=None, stream=None):
         raise ValueError("cache has fewer rows than src")
     _call("kv8_quantize_rows", ctypes.c_void_p(src.data_ptr()), src.stride(0), src.shape[0],
           KV_LORA, ROPE, pc, ps, pd, _stream(stream))
+
+
+def norm_rope_quantize_rows(src, norm_weight, eps, positions, rope_theta, codes, scales,
+                            dst_rows=None, stream=None):
+    """The producer step fused with the quantizer: RMS-normalise the Lc part of
+    each f32 row src [n, >=576] with norm_weight [512] and eps, rotate the Rc
+    pairs by positions [n] (int64 GPU tensor) and rope_theta, and quantize the
+    result into the cache (row i -> cache row dst_rows[i] or i)."""
+    torch = _torch()
+    _check(src, "src", torch.float32, 2, contiguous=False)
+    if src.stride(1) != 1:
+        raise ValueError("src rows must be contiguous")
+    if src.shape[1] < ROW_BYTES:
+        raise ValueError("src rows must hold at least %d values" % ROW_BYTES)
+    pw = _check(norm_weight, "norm_weight", torch.float32, 1)
+    if norm_weight.numel() != KV_LORA:
+        raise ValueError("norm_weight must hold %d values" % KV_LORA)
+    pp = _check(positions, "positions", torch.int64, 1)
+    if positions.numel() != src.shape[0]:
+        raise ValueError("positions must have one entry per source row")
+    pc = _check(codes, "codes", torch.uint8, 2)
+    ps = _check(scales, "scales", torch.float32, 2)
+    if codes.shape[1] != ROW_BYTES or scales.shape[1] != 2 or scales.shape[0] != codes.shape[0]:
+        raise ValueError("cache must be codes [rows, 576] uint8 and scales [rows, 2] f32")
+    pd = None
+    if dst_rows is not None:
+        pd = _check(dst_rows, "dst_rows", torch.int64, 1)
+        if dst_rows.numel() != src.shape[0]:
+            raise ValueError("dst_rows must have one entry per source row")
+    elif src.shape[0] > codes.shape[0]:
+        raise ValueError("cache has fewer rows than src")
+    _call("kv8_norm_rope_quantize_rows", ctypes.c_void_p(src.data_ptr()), src.stride(0),
+          src.shape[0], KV_LORA, ROPE, pw, float(eps), pp, float(rope_theta), pc, ps, pd,
+          _stream(stream))
 
 
 def _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out):

@@ -43,6 +43,26 @@ int kv8_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows, 
                                               static_cast<hipStream_t>(stream)));
 }
 
+int kv8_norm_rope_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
+                                int32_t kv_lora, int32_t rope, const float* norm_weight, float eps,
+                                const int64_t* positions, float rope_theta, uint8_t* codes,
+                                float* scales, const int64_t* dst_rows, void* stream) {
+    if (n_rows < 0) return KV8_EINVAL;
+    if (kv_lora != kv8::kKvLora || rope != kv8::kRope) return KV8_EUNSUPPORTED;
+    if (!(eps >= 0.0f && eps <= 3.0e38f) || !(rope_theta > 0.0f && rope_theta <= 3.0e38f))
+        return KV8_EINVAL;
+    if (n_rows == 0) return KV8_OK;
+    if (!src || !codes || !scales || !norm_weight || !positions) return KV8_EINVAL;
+    if (src_row_stride < kv_lora + rope || src_row_stride % 4 != 0) return KV8_EINVAL;
+    if (!aligned(src, 16) || !aligned(codes, 4) || !aligned(scales, 8) || !aligned(norm_weight, 16) ||
+        !aligned(positions, 8))
+        return KV8_EINVAL;
+    if (dst_rows && !aligned(dst_rows, 8)) return KV8_EINVAL;
+    return launched(kv8::launch_norm_rope_quantize_rows(src, src_row_stride, n_rows, norm_weight, eps,
+                                                        positions, rope_theta, codes, scales, dst_rows,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
 int kv8_encode_bits(uint32_t first, uint64_t count, uint8_t* out, void* stream) {
     if (count == 0) return KV8_OK;
     if (!out || !aligned(out, 4)) return KV8_EINVAL;

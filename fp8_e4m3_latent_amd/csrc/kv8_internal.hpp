@@ -13,6 +13,11 @@ constexpr int kRope = 64;     // supported Rc width
 
 int launch_quantize_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
                          float* scales, const int64_t* dst_rows, hipStream_t stream);
+// the producer step (RMS-normalised Lc, rotary-embedded Rc) fused with the quantizer
+int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_rows,
+                                   const float* norm_weight, float eps, const int64_t* positions,
+                                   float theta, uint8_t* codes, float* scales,
+                                   const int64_t* dst_rows, hipStream_t stream);
 int launch_encode_bits(uint32_t first, uint64_t count, uint8_t* out, hipStream_t stream);
 // One absorbed-decode launch (see kv8_decode.hip).  Token ranges: with
 // split_chunk > 0 range s of a sequence is [s * split_chunk, (s+1) * split_chunk);

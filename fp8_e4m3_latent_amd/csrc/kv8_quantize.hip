@@ -22,6 +22,15 @@
 //   the clamp to [-448, 448] and NaN -> +0, which reproduces the encoder
 //   rules exactly for every f32 value;
 //   the eight scale pairs of a wave are written by eight lanes at once.
+//
+// The producer variant (same page, attention_rows item: the producer
+// quantizes the fresh normalised and rotary-embedded row) first turns the
+// loaded row into y and quantizes y exactly as above:
+//   Lc: y_j = w_j (x_j r), r = 1 / sqrt(sum_k x_k^2 / 512 + eps), the sum of
+//   squares reduced over the wave in f32;
+//   Rc: pairs (2i, 2i+1) rotated by a_i = fl32(fl32(pos) f_i), with the f32
+//   frequency f_i = fl32(theta^(-2i/64)) evaluated in f64 (lane l < 16 holds
+//   pairs 2l and 2l+1), cos and sin from the f32 sincos.
 #include "kv8_device.hpp"
 #include "kv8_internal.hpp"
 
@@ -57,6 +66,20 @@ __device__ __forceinline__ uint32_t wave_max_uniform(uint32_t v) {
     return max(max(r0, r1), max(r2, r3));
 }
 
+// f32 sum over the wave, returned wave-uniform (DPP steps within each row of
+// 16 lanes, then the four row sums)
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 load_stream(const float* p) {  // read-once data
     const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
@@ -82,15 +105,23 @@ __device__ __forceinline__ uint32_t encode4(float4 v, float inv, bool finite) {
 constexpr int kQuantWaves = 4;    // waves per 256-thread block
 constexpr int64_t kFewRows = 8192;  // below: one row per wave
 
+// producer step inputs (unused by the plain quantizer)
+struct ProducerArgs {
+    const float* norm_weight;   // [512]
+    const int64_t* positions;   // [n_rows]
+    float eps;
+    float theta;
+};
+
 // kRowsPerWave rows per wave: 8 for bulk work (eight rows of loads in flight
 // per wave), 1 for a few rows (the per-token append of a decode step, where
 // the kernel's latency is what counts: one row per wave spreads the rows
 // over more compute units and shortens each wave's chain).
-template <int kRowsPerWave>
+template <int kRowsPerWave, bool kProducer>
 __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     const float* __restrict__ src, int64_t stride, int64_t n_rows,
     uint8_t* __restrict__ codes, float* __restrict__ scales,
-    const int64_t* __restrict__ dst_rows) {
+    const int64_t* __restrict__ dst_rows, ProducerArgs pa) {
     constexpr int kSegs = 2 * kRowsPerWave;  // (row, Lc/Rc) segments of a wave
     const int lane = threadIdx.x & 63;
     const int64_t row0 =
@@ -106,6 +137,35 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
         b[r] = load_stream(x + 256 + 4 * lane);
         c[r] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (lane < 16) c[r] = load_stream(x + kKvLora + 4 * lane);
+    }
+
+    if constexpr (kProducer) {
+        // Lc weights of the lane's columns; frequencies of pairs 2 l, 2 l + 1
+        const float4 wa = *reinterpret_cast<const float4*>(pa.norm_weight + 4 * lane);
+        const float4 wb = *reinterpret_cast<const float4*>(pa.norm_weight + 256 + 4 * lane);
+        const float f0 = static_cast<float>(pow(static_cast<double>(pa.theta), -(4.0 * lane) / kRope));
+        const float f1 = static_cast<float>(pow(static_cast<double>(pa.theta), -(4.0 * lane + 2.0) / kRope));
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) {
+            const int64_t row = row0 + r < n_rows ? row0 + r : row0;
+            float4& u = a[r];
+            float4& v = b[r];
+            float ss = u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+            ss = wave_sum_uniform(ss);
+            const float rr = 1.0f / __fsqrt_rn(ss * (1.0f / kKvLora) + pa.eps);
+            u = make_float4(wa.x * (u.x * rr), wa.y * (u.y * rr), wa.z * (u.z * rr), wa.w * (u.w * rr));
+            v = make_float4(wb.x * (v.x * rr), wb.y * (v.y * rr), wb.z * (v.z * rr), wb.w * (v.w * rr));
+            if (lane < 16) {
+                const float pos = static_cast<float>(pa.positions[row]);
+                float s0, c0, s1, c1;
+                sincosf(pos * f0, &s0, &c0);
+                sincosf(pos * f1, &s1, &c1);
+                const float4 q = c[r];
+                c[r] = make_float4(q.x * c0 - q.y * s0, q.x * s0 + q.y * c0,
+                                   q.z * c1 - q.w * s1, q.z * s1 + q.w * c1);
+            }
+        }
     }
 
     // segment k = 2 r + (0: Lc, 1: Rc): amax over finite |x|; the plain
@@ -210,21 +270,36 @@ __global__ __launch_bounds__(256) void decode_codes_kernel(const uint8_t* __rest
 
 }  // namespace
 
-int launch_quantize_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
-                         float* scales, const int64_t* dst_rows, hipStream_t stream) {
+template <bool kProducer>
+int launch_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes, float* scales,
+                const int64_t* dst_rows, const ProducerArgs& pa, hipStream_t stream) {
     if (n_rows < kFewRows) {
         const int64_t blocks = (n_rows + kQuantWaves - 1) / kQuantWaves;
-        hipLaunchKernelGGL(quantize_rows_kernel<1>, dim3(static_cast<uint32_t>(blocks)),
+        hipLaunchKernelGGL((quantize_rows_kernel<1, kProducer>), dim3(static_cast<uint32_t>(blocks)),
                            dim3(64 * kQuantWaves), 0, stream, src, stride, n_rows, codes, scales,
-                           dst_rows);
+                           dst_rows, pa);
     } else {
         const int64_t rows_per_block = static_cast<int64_t>(kQuantWaves) * 8;
         const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
-        hipLaunchKernelGGL(quantize_rows_kernel<8>, dim3(static_cast<uint32_t>(blocks)),
+        hipLaunchKernelGGL((quantize_rows_kernel<8, kProducer>), dim3(static_cast<uint32_t>(blocks)),
                            dim3(64 * kQuantWaves), 0, stream, src, stride, n_rows, codes, scales,
-                           dst_rows);
+                           dst_rows, pa);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_quantize_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
+                         float* scales, const int64_t* dst_rows, hipStream_t stream) {
+    return launch_rows<false>(src, stride, n_rows, codes, scales, dst_rows,
+                              ProducerArgs{nullptr, nullptr, 0.0f, 0.0f}, stream);
+}
+
+int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_rows,
+                                   const float* norm_weight, float eps, const int64_t* positions,
+                                   float theta, uint8_t* codes, float* scales,
+                                   const int64_t* dst_rows, hipStream_t stream) {
+    return launch_rows<true>(src, stride, n_rows, codes, scales, dst_rows,
+                             ProducerArgs{norm_weight, positions, eps, theta}, stream);
 }
 
 int launch_encode_bits(uint32_t first, uint64_t count, uint8_t* out, hipStream_t stream) {

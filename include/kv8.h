@@ -86,6 +86,35 @@ int kv8_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
                       uint8_t* codes, float* scales, const int64_t* dst_rows,
                       void* stream);
 
+/* The producer step fused with the quantizer ([colibri#299] commit message,
+ * attention_rows item: the producer quantizes the fresh normalised and
+ * rotary-embedded latent row in place of the f32 copy).  The page names the
+ * two steps but not their form; this call takes the standard ones:
+ *
+ *   Lc: y_j = w_j x_j / sqrt(mean_k x_k^2 + eps)   (RMS normalisation);
+ *   Rc: the interleaved pairs (2i, 2i+1), i < rope/2, are rotated by the angle
+ *       a_i = fl32(fl32(pos) f_i), f_i = fl32(rope_theta^(-2i/rope)):
+ *       y_2i = x_2i cos a_i - x_2i+1 sin a_i, y_2i+1 = x_2i sin a_i + x_2i+1 cos a_i;
+ *
+ * and y is then quantized and stored exactly as kv8_quantize_rows does with
+ * y for the source row.  y is computed in f32 (sum of squares reduced in f32,
+ * f32 sincos), so a code may differ by one step from the quantization of the
+ * exact y where that value lies next to a rounding boundary.
+ *
+ * src, src_row_stride, n_rows, codes, scales, dst_rows   as kv8_quantize_rows.
+ * norm_weight    f32 [kv_lora] device array, 16-byte aligned.
+ * eps            >= 0 and finite.
+ * positions      int64 [n_rows] device array, 8-byte aligned: the token
+ *                position of each row.
+ * rope_theta     > 0 and finite (e.g. 10000).
+ * Returns KV8_EINVAL for a bad argument, KV8_EUNSUPPORTED unless kv_lora is
+ * 512 and rope 64, KV8_ELAUNCH when the launch fails. */
+int kv8_norm_rope_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
+                                int32_t kv_lora, int32_t rope, const float* norm_weight,
+                                float eps, const int64_t* positions, float rope_theta,
+                                uint8_t* codes, float* scales, const int64_t* dst_rows,
+                                void* stream);
+
 /* Absorbed-MLA decode straight from the fp8 rows ([colibri#299] commit
  * message, first paragraph and attention_rows item).
  *

@@ -21,7 +21,8 @@ of that kernel alone, back to back on the same rotating caches (the per-step
 events around it also hold its dispatch gap behind the append kernel).
 
 Other legs (same JSON line, key "legs"): the bulk quantizer (32,768 tokens x
-61 layers of Student-t rows with planted special rows), the 256k-token
+61 layers of Student-t rows with planted special rows; the same rows also
+through the producer step fused with the quantizer), the 256k-token
 split-T decode with 64 ranges, and the ragged Q=4 multi-query decode.
 
 The CPU baseline is the oracle (oracle/, test infrastructure) timed on a
@@ -218,12 +219,28 @@ def leg_quantize(torch, kv8, W, steps):
     torch.cuda.synchronize()
     ms = float(timer.intervals_ms()[:, 0].mean())
     nbytes = float(n) * (4 * D + D + 8)
-    del rows, codes, scales
+    res = {"rows": n, "ms": ms, "rows_per_s": n / (ms * 1e-3),
+           "gb_per_s": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes,
+           "roofline": roofline_hbm(nbytes, ms, counter_traffic("quantize_rows_kernel",
+                                                                "kv8_quantize.hip"))}
+    # the producer step fused with the quantizer on the same rows: RMS norm of
+    # Lc (seeded weight, eps 1e-6), rotation of the Rc pairs at the row's token
+    # position (row index mod 32768, base 10000); 8 more bytes a row (position)
+    g = np.random.default_rng(5)
+    wgt = torch.from_numpy(g.uniform(0.25, 2.0, KL).astype(np.float32)).to("cuda")
+    pos = torch.arange(n, dtype=torch.int64, device="cuda") % 32768
+    prod = lambda: kv8.norm_rope_quantize_rows(rows, wgt, 1e-6, pos, 10000.0, codes, scales)
+    for _ in range(2):
+        prod()
+    torch.cuda.synchronize()
+    pms = timer_call(torch, steps, prod)
+    pbytes = float(n) * (4 * D + 8 + D + 8)
+    res["producer"] = {"rows": n, "ms": pms, "rows_per_s": n / (pms * 1e-3),
+                       "gb_per_s": pbytes / (pms * 1e-3) / 1e9, "bytes_per_launch": pbytes,
+                       "roofline": roofline_hbm(pbytes, pms, None)}
+    del rows, codes, scales, pos
     torch.cuda.empty_cache()
-    return {"rows": n, "ms": ms, "rows_per_s": n / (ms * 1e-3),
-            "gb_per_s": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes,
-            "roofline": roofline_hbm(nbytes, ms, counter_traffic("quantize_rows_kernel",
-                                                                 "kv8_quantize.hip"))}
+    return res
 
 
 def _decode_workload_leg(torch, kv8, w, steps, splits=None):

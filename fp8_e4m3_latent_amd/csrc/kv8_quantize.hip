@@ -29,8 +29,11 @@
 //   Lc: y_j = w_j (x_j r), r = 1 / sqrt(sum_k x_k^2 / 512 + eps), the sum of
 //   squares reduced over the wave in f32;
 //   Rc: pairs (2i, 2i+1) rotated by a_i = fl32(fl32(pos) f_i), with the f32
-//   frequency f_i = fl32(theta^(-2i/64)) evaluated in f64 (lane l < 16 holds
-//   pairs 2l and 2l+1), cos and sin from the f32 sincos.
+//   frequency f_i = fl32(theta^(-2i/64)) evaluated in f64 on the host (lane
+//   l < 16 holds pairs 2l and 2l+1); a_i is reduced modulo 2 pi in f64 and
+//   cos and sin come from the f32 sincos of the reduced angle.
+#include <cmath>
+
 #include "kv8_device.hpp"
 #include "kv8_internal.hpp"
 
@@ -80,6 +83,20 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// a - 2 pi k in [-pi, pi] for an f32 angle a, reduced in f64 (2 pi as a sum of
+// two doubles, so the reduction is exact to ~1e-16 for |a| < 2^40) and rounded
+// to f32: sincosf then stays on its short path.  The f32 rounding of the
+// reduced angle adds at most 2^-23 to it.
+__device__ __forceinline__ float reduce_angle(float a) {
+    const double two_pi_hi = 6.283185307179586232;    // fl64(2 pi)
+    const double two_pi_lo = 2.4492935982947064e-16;  // 2 pi - two_pi_hi
+    const double x = static_cast<double>(a);
+    const double k = rint(x * (1.0 / 6.283185307179586232));
+    double r = fma(-k, two_pi_hi, x);
+    r = fma(-k, two_pi_lo, r);
+    return static_cast<float>(r);
+}
+
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 load_stream(const float* p) {  // read-once data
     const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
@@ -110,7 +127,7 @@ struct ProducerArgs {
     const float* norm_weight;   // [512]
     const int64_t* positions;   // [n_rows]
     float eps;
-    float theta;
+    float freq[kRope / 2];      // f_i = fl32(theta^(-2i/64)), from the host
 };
 
 // kRowsPerWave rows per wave: 8 for bulk work (eight rows of loads in flight
@@ -143,8 +160,8 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
         // Lc weights of the lane's columns; frequencies of pairs 2 l, 2 l + 1
         const float4 wa = *reinterpret_cast<const float4*>(pa.norm_weight + 4 * lane);
         const float4 wb = *reinterpret_cast<const float4*>(pa.norm_weight + 256 + 4 * lane);
-        const float f0 = static_cast<float>(pow(static_cast<double>(pa.theta), -(4.0 * lane) / kRope));
-        const float f1 = static_cast<float>(pow(static_cast<double>(pa.theta), -(4.0 * lane + 2.0) / kRope));
+        const float f0 = pa.freq[2 * (lane & 15)];
+        const float f1 = pa.freq[2 * (lane & 15) + 1];
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
             const int64_t row = row0 + r < n_rows ? row0 + r : row0;
@@ -159,8 +176,8 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
             if (lane < 16) {
                 const float pos = static_cast<float>(pa.positions[row]);
                 float s0, c0, s1, c1;
-                sincosf(pos * f0, &s0, &c0);
-                sincosf(pos * f1, &s1, &c1);
+                sincosf(reduce_angle(pos * f0), &s0, &c0);
+                sincosf(reduce_angle(pos * f1), &s1, &c1);
                 const float4 q = c[r];
                 c[r] = make_float4(q.x * c0 - q.y * s0, q.x * s0 + q.y * c0,
                                    q.z * c1 - q.w * s1, q.z * s1 + q.w * c1);
@@ -291,15 +308,17 @@ int launch_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes
 int launch_quantize_rows(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
                          float* scales, const int64_t* dst_rows, hipStream_t stream) {
     return launch_rows<false>(src, stride, n_rows, codes, scales, dst_rows,
-                              ProducerArgs{nullptr, nullptr, 0.0f, 0.0f}, stream);
+                              ProducerArgs{nullptr, nullptr, 0.0f, {}}, stream);
 }
 
 int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_rows,
                                    const float* norm_weight, float eps, const int64_t* positions,
                                    float theta, uint8_t* codes, float* scales,
                                    const int64_t* dst_rows, hipStream_t stream) {
-    return launch_rows<true>(src, stride, n_rows, codes, scales, dst_rows,
-                             ProducerArgs{norm_weight, positions, eps, theta}, stream);
+    ProducerArgs pa{norm_weight, positions, eps, {}};
+    for (int i = 0; i < kRope / 2; ++i)
+        pa.freq[i] = static_cast<float>(std::pow(static_cast<double>(theta), -2.0 * i / kRope));
+    return launch_rows<true>(src, stride, n_rows, codes, scales, dst_rows, pa, stream);
 }
 
 int launch_encode_bits(uint32_t first, uint64_t count, uint8_t* out, hipStream_t stream) {

@@ -147,8 +147,10 @@ def test_producer_scatter_and_stride(kv8):
 
 
 def test_producer_special_rows_exact(kv8):
-    """NaN, inf and zero rows, and eps = 0 on a zero row (0/0): results the f32
-    rounding cannot change, bit for bit."""
+    """NaN, inf and zero rows, and eps = 0 on a zero row (0/0): the segments
+    whose result the f32 rounding cannot change match bit for bit (an inf or
+    NaN in Lc turns the whole segment into zeros or NaN; an inf in Rc
+    saturates its own pair only)."""
     x, w, pos = inputs(9, 6)
     x[0, :] = 0.0
     x[1, 5] = np.nan
@@ -162,9 +164,12 @@ def test_producer_special_rows_exact(kv8):
         for r in (0, 1, 2, 5):      # Lc segments
             assert np.array_equal(gc[r, :KL], oc[r, :KL]), (eps, r)
             assert gs[r, 0].view(np.uint32) == os_[r, 0].view(np.uint32), (eps, r)
-        for r in (3, 4):            # Rc segments with inf / NaN
-            assert np.array_equal(gc[r, KL:], oc[r, KL:]), (eps, r)
-            assert gs[r, 1].view(np.uint32) == os_[r, 1].view(np.uint32), (eps, r)
+        # Rc all NaN: codes 0, guarded scale 0
+        assert not gc[4, KL:].any() and gs[4, 1] == 0 and not oc[4, KL:].any() and os_[4, 1] == 0
+        # Rc with -inf in pair 1: that pair saturates; the other pairs (which set
+        # the scale) are ordinary rotated values, compared to the general bar
+        assert np.array_equal(gc[3, KL + 2:KL + 4], oc[3, KL + 2:KL + 4]), eps
+        compare(x[3:4], y[3:4], gc[3:4], gs[3:4], oc[3:4], os_[3:4])
 
 
 def test_producer_position_zero_equals_plain_quantizer_on_rc(kv8):

@@ -31,7 +31,9 @@
 //   Rc: pairs (2i, 2i+1) rotated by a_i = fl32(fl32(pos) f_i), with the f32
 //   frequency f_i = fl32(theta^(-2i/64)) evaluated in f64 on the host (lane
 //   l < 16 holds pairs 2l and 2l+1); a_i is reduced modulo 2 pi in f64 and
-//   cos and sin come from the f32 sincos of the reduced angle.
+//   cos and sin come from the f32 sincos of the reduced angle (with eight rows
+//   a wave, every lane computes four of the wave's 256 rotations and passes
+//   them on through LDS).
 #include <cmath>
 
 #include "kv8_device.hpp"
@@ -162,6 +164,23 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
         const float4 wb = *reinterpret_cast<const float4*>(pa.norm_weight + 256 + 4 * lane);
         const float f0 = pa.freq[2 * (lane & 15)];
         const float f1 = pa.freq[2 * (lane & 15) + 1];
+        // With eight rows, the 8 x 32 rotations of the wave are spread over all
+        // lanes: lane L computes (cos, sin) of pairs 4 (L % 8) .. +3 of row L / 8
+        // into this wave's LDS area, [row][pair][cos, sin], where lane l < 16
+        // (the Rc holder of pairs 2 l, 2 l + 1) reads them.
+        float* rot = nullptr;
+        if constexpr (kRowsPerWave == 8) {
+            __shared__ __attribute__((aligned(16))) float s_rot[kQuantWaves][8 * 32 * 2];
+            rot = &s_rot[threadIdx.x >> 6][0];
+            const int64_t rrow = row0 + (lane >> 3) < n_rows ? row0 + (lane >> 3) : row0;
+            const float rpos = static_cast<float>(pa.positions[rrow]);
+            float cv[4], sv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                sincosf(reduce_angle(rpos * pa.freq[4 * (lane & 7) + t]), &sv[t], &cv[t]);
+            *reinterpret_cast<float4*>(rot + 8 * lane) = make_float4(cv[0], sv[0], cv[1], sv[1]);
+            *reinterpret_cast<float4*>(rot + 8 * lane + 4) = make_float4(cv[2], sv[2], cv[3], sv[3]);
+        }
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
             const int64_t row = row0 + r < n_rows ? row0 + r : row0;
@@ -174,10 +193,15 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
             u = make_float4(wa.x * (u.x * rr), wa.y * (u.y * rr), wa.z * (u.z * rr), wa.w * (u.w * rr));
             v = make_float4(wb.x * (v.x * rr), wb.y * (v.y * rr), wb.z * (v.z * rr), wb.w * (v.w * rr));
             if (lane < 16) {
-                const float pos = static_cast<float>(pa.positions[row]);
                 float s0, c0, s1, c1;
-                sincosf(reduce_angle(pos * f0), &s0, &c0);
-                sincosf(reduce_angle(pos * f1), &s1, &c1);
+                if constexpr (kRowsPerWave == 8) {
+                    const float4 t = *reinterpret_cast<const float4*>(rot + 64 * r + 4 * lane);
+                    c0 = t.x; s0 = t.y; c1 = t.z; s1 = t.w;
+                } else {
+                    const float pos = static_cast<float>(pa.positions[row]);
+                    sincosf(reduce_angle(pos * f0), &s0, &c0);
+                    sincosf(reduce_angle(pos * f1), &s1, &c1);
+                }
                 const float4 q = c[r];
                 c[r] = make_float4(q.x * c0 - q.y * s0, q.x * s0 + q.y * c0,
                                    q.z * c1 - q.w * s1, q.z * s1 + q.w * c1);

@@ -237,7 +237,8 @@ def leg_quantize(torch, kv8, W, steps):
     pbytes = float(n) * (4 * D + 8 + D + 8)
     res["producer"] = {"rows": n, "ms": pms, "rows_per_s": n / (pms * 1e-3),
                        "gb_per_s": pbytes / (pms * 1e-3) / 1e9, "bytes_per_launch": pbytes,
-                       "roofline": roofline_hbm(pbytes, pms, None)}
+                       "roofline": roofline_hbm(pbytes, pms, counter_traffic("norm_rope_quantize_rows",
+                                                                            "kv8_quantize.hip"))}
     del rows, codes, scales, pos
     torch.cuda.empty_cache()
     return res

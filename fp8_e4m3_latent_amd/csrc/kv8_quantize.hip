@@ -26,8 +26,9 @@
 // The producer variant (same page, attention_rows item: the producer
 // quantizes the fresh normalised and rotary-embedded row) first turns the
 // loaded row into y and quantizes y exactly as above:
-//   Lc: y_j = w_j (x_j r), r = 1 / sqrt(sum_k x_k^2 / 512 + eps), the sum of
-//   squares reduced over the wave in f32;
+//   Lc: y_j = w_j (x_j r), r = 1 / sqrt(sum_k x_k^2 / 512 + eps) from the
+//   hardware reciprocal square root, the sum of squares reduced over the wave
+//   in f32;
 //   Rc: pairs (2i, 2i+1) rotated by a_i = fl32(fl32(pos) f_i), with the f32
 //   frequency f_i = fl32(theta^(-2i/64)) evaluated in f64 on the host (lane
 //   l < 16 holds pairs 2l and 2l+1); a_i is reduced modulo 2 pi in f64 and
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
             float ss = u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
             ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
             ss = wave_sum_uniform(ss);
-            const float rr = 1.0f / __fsqrt_rn(ss * (1.0f / kKvLora) + pa.eps);
+            const float rr = __builtin_amdgcn_rsqf(ss * (1.0f / kKvLora) + pa.eps);  // (~1 ulp)
             u = make_float4(wa.x * (u.x * rr), wa.y * (u.y * rr), wa.z * (u.z * rr), wa.w * (u.w * rr));
             v = make_float4(wb.x * (v.x * rr), wb.y * (v.y * rr), wb.z * (v.z * rr), wb.w * (v.w * rr));
             if (lane < 16) {

@@ -57,6 +57,9 @@ def lib():
     L.orc_norm_rope_rows.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                      ctypes.c_int32, _f32p, ctypes.c_float, _i64p, ctypes.c_float,
                                      _f32p, ctypes.c_int]
+    L.orc_project_rows.restype = None
+    L.orc_project_rows.argtypes = [_u8p, _f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                   _u16p, ctypes.c_int32, _f64p, _f64p, ctypes.c_int]
     L.orc_bytes_per_token_layer.restype = ctypes.c_int64
     L.orc_bytes_per_token_layer.argtypes = [ctypes.c_int32, ctypes.c_int32]
     _lib = L
@@ -146,6 +149,21 @@ def norm_rope_rows(src, norm_weight, eps, positions, rope_theta, kv_lora=512, ro
                              float(eps), _p(pos, _i64p), float(rope_theta), _p(out, _f32p),
                              _t(threads))
     return out
+
+
+def project_rows(codes, scales, w_bf16, kv_lora=512, rope=64, threads=0):
+    """Non-absorbed projection of cache rows: out f64 [n, N] = s_Lc * dec(Lc) @ W^T
+    with W bf16 bits [N, kv_lora]; rope f64 [n, rope] = s_Rc * dec(Rc)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.float32)
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, N = c.shape[0], w.shape[0]
+    assert c.shape[1] == kv_lora + rope and s.shape == (n, 2) and w.shape[1] == kv_lora
+    out = np.empty((n, N), dtype=np.float64)
+    rp = np.empty((n, rope), dtype=np.float64)
+    lib().orc_project_rows(_p(c, _u8p), _p(s, _f32p), n, kv_lora, rope, _p(w, _u16p), N,
+                           _p(out, _f64p), _p(rp, _f64p), _t(threads))
+    return out, rp
 
 
 def _attn_common(q_lat, q_rope, kv_start, kv_len, Q, sel):

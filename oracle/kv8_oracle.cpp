@@ -364,6 +364,36 @@ void orc_norm_rope_rows(const float* src, int64_t src_row_stride, int64_t n_rows
     });
 }
 
+// [colibri#299] commit message, attention_rows item: the non-absorbed prefill
+// dequantizes Lc (code value times the row's Lc scale) and multiplies it by the
+// kv_b weight; Rc is read through the decode table.  The row scale is applied
+// to each product here, as the dequantized staging row holds it.
+void orc_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
+                      int32_t kv_lora, int32_t rope, const uint16_t* w_bf16, int32_t N,
+                      double* out, double* rope_out, int threads) {
+    const int64_t d = static_cast<int64_t>(kv_lora) + rope;
+    std::vector<double> w(static_cast<size_t>(N) * kv_lora);
+    for (size_t i = 0; i < w.size(); ++i) {
+        const uint32_t bits = static_cast<uint32_t>(w_bf16[i]) << 16;
+        float f;
+        std::memcpy(&f, &bits, 4);
+        w[i] = f;
+    }
+    const Tables& t = tables();
+    parallel_for(n_rows, threads, [&](int64_t m) {
+        const uint8_t* c = codes + m * d;
+        std::vector<double> x(static_cast<size_t>(kv_lora));
+        for (int32_t k = 0; k < kv_lora; ++k) x[static_cast<size_t>(k)] = t.all[c[k]] * scales[2 * m];
+        for (int32_t n = 0; n < N; ++n) {
+            const double* wn = w.data() + static_cast<size_t>(n) * kv_lora;
+            double acc = 0.0;
+            for (int32_t k = 0; k < kv_lora; ++k) acc += x[static_cast<size_t>(k)] * wn[k];
+            out[m * N + n] = acc;
+        }
+        for (int32_t j = 0; j < rope; ++j) rope_out[m * rope + j] = t.all[c[kv_lora + j]] * scales[2 * m + 1];
+    });
+}
+
 int64_t orc_bytes_per_token_layer(int32_t kv_lora, int32_t rope) {
     return static_cast<int64_t>(kv_lora) + rope + 2 * static_cast<int64_t>(sizeof(float));
 }

@@ -92,6 +92,18 @@ void orc_norm_rope_rows(const float* src, int64_t src_row_stride, int64_t n_rows
                         int32_t kv_lora, int32_t rope, const float* norm_weight, float eps,
                         const int64_t* positions, float rope_theta, float* out, int threads);
 
+/* The non-absorbed consumer of the same rows ([colibri#299] commit message,
+ * attention_rows item: the non-absorbed prefill dequantizes Lc into a staging
+ * row for the kv_b matmul and reads Rc through the decode table), in f64:
+ *   out[m][n]  = s_Lc[m] * sum_k decode(code[m][k]) * W[n][k],  k < kv_lora,
+ *   rope[m][j] = s_Rc[m] * decode(code[m][kv_lora + j]),       j < rope,
+ * for the n_rows cache rows codes[0..n_rows), scales[0..n_rows) and a bf16
+ * weight W[N][kv_lora] (bits; row n holds output column n's weights, the
+ * layout of a linear layer's weight). */
+void orc_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
+                      int32_t kv_lora, int32_t rope, const uint16_t* w_bf16, int32_t N,
+                      double* out, double* rope_out, int threads);
+
 /* Bytes one token occupies per layer: kv_lora + rope code bytes plus the two
  * f32 scales ([colibri#299] PR description: one f32 scale each for Lc, Rc). */
 int64_t orc_bytes_per_token_layer(int32_t kv_lora, int32_t rope);

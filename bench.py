@@ -281,6 +281,35 @@ def _decode_workload_leg(torch, kv8, w, steps, splits=None):
                             "gb_per_s": qbytes / (qt * 1e-3) / 1e9}}
 
 
+def leg_project(torch, kv8, steps):
+    """Non-absorbed projection of one 8,192-token sequence's cache rows by a
+    bf16 kv_b weight of N = 128 heads x (128 + 128) columns (random weights)."""
+    n, N = 8192, 32768
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    rows = torch.randn((n, D), generator=g, device="cuda")
+    codes = torch.empty((n, D), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, 2), dtype=torch.float32, device="cuda")
+    kv8.quantize_rows(rows, codes, scales)
+    del rows
+    w = (torch.randn((N, KL), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+    out = torch.empty((n, N), dtype=torch.bfloat16, device="cuda")
+    rope = torch.empty((n, KR), dtype=torch.float32, device="cuda")
+    fn = lambda: kv8.project_rows(codes, scales, w, out=out, rope_out=rope)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ms = timer_call(torch, steps, fn)
+    flops = 2.0 * n * KL * N
+    nbytes = float(n) * (D + 8) + 2.0 * N * KL + 2.0 * n * N + 4.0 * n * KR
+    ach = flops / (ms * 1e-3) / 1e12
+    del codes, scales, w, out, rope
+    torch.cuda.empty_cache()
+    return {"rows": n, "N": N, "ms": ms, "tflops": ach, "gb_per_s": nbytes / (ms * 1e-3) / 1e9,
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}}
+
+
 def leg_copy(torch, steps):
     """Plain 1 GiB device copy: the reference for scaling HBM byte counters."""
     n = 1 << 28
@@ -316,8 +345,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--legs", default="decode,quantize,splitT",
-                    help="comma list of decode, quantize, splitT, ragged, copy")
+    ap.add_argument("--legs", default="decode,quantize,splitT,project",
+                    help="comma list of decode, quantize, splitT, project, ragged, copy")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096,
                     help="query rows the oracle times for the CPU baseline (0: skip)")
     args = ap.parse_args()
@@ -351,6 +380,9 @@ def main():
         log("splitT: 256k-token slot, 64 ranges")
         extra["splitT_256k"] = _decode_workload_leg(torch, kv8, W.long_context(seed=0),
                                                     max(5, args.steps // 2), splits=64)
+    if "project" in legs:
+        log("project: 8192 rows x N=32768")
+        extra["project_8k"] = leg_project(torch, kv8, max(5, args.steps // 4))
     if "copy" in legs:
         extra["copy_1gib"] = leg_copy(torch, 3)
     if "ragged" in legs:

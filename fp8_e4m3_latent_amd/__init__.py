@@ -24,7 +24,7 @@ _STATUS = {0: "KV8_OK", -1: "KV8_EINVAL", -2: "KV8_EUNSUPPORTED", -3: "KV8_ELAUN
            -4: "KV8_EWORKSPACE", -5: "KV8_ENOMEM"}
 
 # every symbol include/kv8.h declares
-EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
+EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_project_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
            "kv8_absorb_decode_splitT", "kv8_partials_bytes", "kv8_decode_plan",
            "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
            "kv8_encode_bits", "kv8_decode_codes")
@@ -54,6 +54,8 @@ def lib():
     L.kv8_status_string.argtypes = [ctypes.c_int]
     L.kv8_quantize_rows.restype = ctypes.c_int
     L.kv8_quantize_rows.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+    L.kv8_project_rows.restype = ctypes.c_int
+    L.kv8_project_rows.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, vp, vp]
     L.kv8_norm_rope_quantize_rows.restype = ctypes.c_int
     L.kv8_norm_rope_quantize_rows.argtypes = [vp, i64, i64, i32, i32, vp, f32, vp, f32, vp, vp,
                                               vp, vp]
@@ -168,6 +170,39 @@ def norm_rope_quantize_rows(src, norm_weight, eps, positions, rope_theta, codes,
     _call("kv8_norm_rope_quantize_rows", ctypes.c_void_p(src.data_ptr()), src.stride(0),
           src.shape[0], KV_LORA, ROPE, pw, float(eps), pp, float(rope_theta), pc, ps, pd,
           _stream(stream))
+
+
+def project_rows(codes, scales, w_kv_b, out=None, rope_out=None, with_rope=True, stream=None):
+    """Non-absorbed projection of the cache rows codes [n, 576] / scales [n, 2]
+    (a contiguous slice of the cache): out bf16 [n, N] = s_Lc * dec(Lc) @ W^T
+    for the bf16 weight w_kv_b [N, 512]; rope_out f32 [n, 64] = s_Rc * dec(Rc).
+    Returns (out, rope_out) (rope_out None when with_rope is False)."""
+    torch = _torch()
+    pc = _check(codes, "codes", torch.uint8, 2)
+    ps = _check(scales, "scales", torch.float32, 2)
+    n = codes.shape[0]
+    if codes.shape[1] != ROW_BYTES or tuple(scales.shape) != (n, 2):
+        raise ValueError("codes must be [n, 576] uint8 and scales [n, 2] f32")
+    pw = _check(w_kv_b, "w_kv_b", torch.bfloat16, 2)
+    N = w_kv_b.shape[0]
+    if w_kv_b.shape[1] != KV_LORA:
+        raise ValueError("w_kv_b must be [N, 512]")
+    if out is None:
+        out = torch.empty((n, N), dtype=torch.bfloat16, device=codes.device)
+    po = _check(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (n, N):
+        raise ValueError("out must be [n, N]")
+    pr = None
+    if with_rope:
+        if rope_out is None:
+            rope_out = torch.empty((n, ROPE), dtype=torch.float32, device=codes.device)
+        pr = _check(rope_out, "rope_out", torch.float32, 2)
+        if tuple(rope_out.shape) != (n, ROPE):
+            raise ValueError("rope_out must be [n, 64]")
+    else:
+        rope_out = None
+    _call("kv8_project_rows", pc, ps, n, KV_LORA, ROPE, pw, N, po, pr, _stream(stream))
+    return out, rope_out
 
 
 def _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out):

@@ -63,6 +63,22 @@ int kv8_norm_rope_quantize_rows(const float* src, int64_t src_row_stride, int64_
                                                         static_cast<hipStream_t>(stream)));
 }
 
+int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, int32_t kv_lora,
+                     int32_t rope, const uint16_t* w_kv_b, int32_t N, uint16_t* out,
+                     float* rope_out, void* stream) {
+    if (n_rows < 0 || N < 0) return KV8_EINVAL;
+    if (kv_lora != kv8::kKvLora || rope != kv8::kRope) return KV8_EUNSUPPORTED;
+    if (N % 128 != 0) return KV8_EUNSUPPORTED;
+    if (n_rows == 0 || N == 0) return KV8_OK;
+    if (!codes || !scales || !w_kv_b || !out) return KV8_EINVAL;
+    if (!aligned(codes, 16) || !aligned(scales, 8) || !aligned(w_kv_b, 16) || !aligned(out, 2) ||
+        (rope_out && !aligned(rope_out, 16)))
+        return KV8_EINVAL;
+    if ((n_rows + 127) / 128 * (N / 128) > (int64_t(1) << 31) - 1) return KV8_EUNSUPPORTED;
+    return launched(kv8::launch_project_rows(codes, scales, n_rows, w_kv_b, N, out, rope_out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int kv8_encode_bits(uint32_t first, uint64_t count, uint8_t* out, void* stream) {
     if (count == 0) return KV8_OK;
     if (!out || !aligned(out, 4)) return KV8_EINVAL;

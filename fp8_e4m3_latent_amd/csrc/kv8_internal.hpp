@@ -19,6 +19,10 @@ int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_r
                                    float theta, uint8_t* codes, float* scales,
                                    const int64_t* dst_rows, hipStream_t stream);
 int launch_encode_bits(uint32_t first, uint64_t count, uint8_t* out, hipStream_t stream);
+// non-absorbed projection of cache rows (see kv8_project.hip); N a multiple of 128
+int launch_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
+                        const uint16_t* w_kv_b, int N, uint16_t* out, float* rope_out,
+                        hipStream_t stream);
 // One absorbed-decode launch (see kv8_decode.hip).  Token ranges: with
 // split_chunk > 0 range s of a sequence is [s * split_chunk, (s+1) * split_chunk);
 // otherwise the sequence is cut into n_outer equal ranges of ceil(L / n_outer)

@@ -209,6 +209,28 @@ int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
 int kv8_lse_merge(const void* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
                   int32_t num_splits, float softmax_scale, float* out, void* stream);
 
+/* The non-absorbed consumer of the cache rows ([colibri#299] commit message,
+ * attention_rows item: the non-absorbed prefill dequantizes Lc into a staging
+ * row for the kv_b matmul and reads Rc via the decode table):
+ *
+ *   out[m][n]      = bf16( s_Lc[m] * sum_k decode(codes[m][k]) * W[n][k] ),  k < kv_lora
+ *   rope_out[m][j] = s_Rc[m] * decode(codes[m][kv_lora + j]),               j < rope
+ *
+ * codes, scales  n_rows consecutive cache rows (layout above), codes 16-byte
+ *                aligned (pass the cache pointers offset to the first row).
+ * w_kv_b         bf16 [N][kv_lora] device array, 16-byte aligned: row n holds
+ *                output column n's weights (a linear layer's weight layout).
+ * N              output columns, a multiple of 128 (KV8_EUNSUPPORTED otherwise).
+ * out            bf16 [n_rows][N]; the products are summed in f32 (bf16 MFMA;
+ *                every e4m3 value is exact in bf16) and the scaled sum is
+ *                rounded to nearest even.
+ * rope_out       f32 [n_rows][rope], 16-byte aligned, or NULL to skip.
+ * Returns KV8_EINVAL for a bad argument, KV8_EUNSUPPORTED unless kv_lora is 512,
+ * rope 64 and N a multiple of 128, KV8_ELAUNCH when the launch fails. */
+int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, int32_t kv_lora,
+                     int32_t rope, const uint16_t* w_kv_b, int32_t N, uint16_t* out,
+                     float* rope_out, void* stream);
+
 /* Human-readable name of a kv8_status value (static string, never NULL). */
 const char* kv8_status_string(int status);
 

@@ -1,0 +1,116 @@
+"""GPU parity of kv8_project_rows (non-absorbed projection of fp8 cache rows)
+against the oracle's project_rows.
+
+Page: "KV8=1: fp8 e4m3 latent KV cache (CPU + CUDA) with .coli_kv v2"
+(colibri PR #299), commit message, attention_rows item.
+
+The kernel sums bf16 x bf16 products in f32 (every e4m3 value is exact in
+bf16) and rounds the scaled sum to bf16; the oracle sums in f64.  Bar per
+element: |gpu - ref| <= 2^-8 |ref| + 2^-20 s_Lc sum_k |dec(c_k)| |W_nk| (one bf16
+rounding plus the f32 accumulation of 512 products).  The dequantized Rc
+(one f32 product of exact values) must equal the oracle's value rounded to
+f32, bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+KL, KR, D = 512, 64, 576
+
+
+@pytest.fixture(scope="module")
+def kv8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_e4m3_latent_amd as m
+    m.lib()
+    return m
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def gpu_cache(kv8, n, seed):
+    x = np.random.default_rng(seed).standard_normal((n, D)).astype(np.float32)
+    x[::7, :KL] *= np.float32(30.0)            # rows of very different scales
+    codes = torch.empty((n, D), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, 2), dtype=torch.float32, device="cuda")
+    kv8.quantize_rows(torch.from_numpy(x).cuda(), codes, scales)
+    torch.cuda.synchronize()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    rc, rs = oracle.quantize_rows(x)
+    assert np.array_equal(c, rc) and np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    return codes, scales, c, s
+
+
+def weights(N, seed):
+    w = torch.from_numpy(np.random.default_rng(seed).standard_normal((N, KL)).astype(np.float32) * 0.05)
+    wb = w.to(torch.bfloat16)
+    return wb.cuda(), wb.view(torch.int16).numpy().view(np.uint16)
+
+
+def check(c, s, wbits, rows, got, got_rope):
+    ref, rref = oracle.project_rows(c[rows], s[rows], wbits)
+    g = got.float().cpu().numpy().astype(np.float64)[rows] if got.shape[0] != len(rows) else got.float().cpu().numpy().astype(np.float64)
+    x = np.abs(oracle.decode(c[rows, :KL])) * s[rows, :1].astype(np.float64)
+    wv = np.abs((wbits.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -20 * (x @ wv.T)
+    err = np.abs(g - ref)
+    assert np.all(err <= bound), "max err/bound %.3f" % float(np.max(err / np.maximum(bound, 1e-300)))
+    if got_rope is not None:
+        gr = got_rope.cpu().numpy()
+        gr = gr[rows] if gr.shape[0] != len(rows) else gr
+        assert np.array_equal(gr.view(np.uint32), rref.astype(np.float32).view(np.uint32))
+    return float(np.max(err / np.maximum(np.abs(ref).max(), 1e-300)))
+
+
+@pytest.mark.parametrize("n,N", [(1, 128), (100, 256), (300, 384), (1000, 128)])
+def test_project_small(kv8, n, N):
+    """Row counts below, at and across the 128-row tile, several column tiles."""
+    say("project: n=%d N=%d" % (n, N))
+    codes, scales, c, s = gpu_cache(kv8, n, 40 + n)
+    wb, wbits = weights(N, 41 + N)
+    out, rope = kv8.project_rows(codes, scales, wb)
+    torch.cuda.synchronize()
+    e = check(c, s, wbits, np.arange(n), out, rope)
+    say("  max |err| / max |ref| = %.2e" % e)
+
+
+def test_project_slice_of_cache_and_no_rope(kv8):
+    """A slice starting at a nonzero cache row; no Rc output requested."""
+    codes, scales, c, s = gpu_cache(kv8, 700, 50)
+    wb, wbits = weights(256, 51)
+    out, rope = kv8.project_rows(codes[200:530], scales[200:530], wb, with_rope=False)
+    torch.cuda.synchronize()
+    assert rope is None
+    check(c[200:530], s[200:530], wbits, np.arange(330), out, None)
+
+
+def test_project_full_size_sampled(kv8):
+    """8,192 rows (one 8k-token sequence) x N = 32,768 (128 heads x (128 + 128)),
+    compared on 48 sampled rows over every column."""
+    n, N = 8192, 32768
+    say("project: full size n=%d N=%d" % (n, N))
+    codes, scales, c, s = gpu_cache(kv8, n, 52)
+    wb, wbits = weights(N, 53)
+    out, rope = kv8.project_rows(codes, scales, wb)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(54).choice(n, 48, replace=False))
+    ot = out[torch.from_numpy(rows).cuda()]
+    rt = rope[torch.from_numpy(rows).cuda()]
+    e = check(c, s, wbits, rows, ot, rt)
+    say("  max |err| / max |ref| = %.2e" % e)
+
+
+def test_project_argument_errors(kv8):
+    codes, scales, _, _ = gpu_cache(kv8, 4, 55)
+    wb, _ = weights(100, 56)      # N not a multiple of 128
+    with pytest.raises(kv8.Kv8Error):
+        kv8.project_rows(codes, scales, wb)
+    with pytest.raises(ValueError):
+        kv8.project_rows(codes, scales[:3], weights(128, 57)[0])

@@ -71,7 +71,7 @@ int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, 
     if (N % 128 != 0) return KV8_EUNSUPPORTED;
     if (n_rows == 0 || N == 0) return KV8_OK;
     if (!codes || !scales || !w_kv_b || !out) return KV8_EINVAL;
-    if (!aligned(codes, 16) || !aligned(scales, 8) || !aligned(w_kv_b, 16) || !aligned(out, 2) ||
+    if (!aligned(codes, 16) || !aligned(scales, 8) || !aligned(w_kv_b, 16) || !aligned(out, 16) ||
         (rope_out && !aligned(rope_out, 16)))
         return KV8_EINVAL;
     if ((n_rows + 127) / 128 * (N / 128) > (int64_t(1) << 31) - 1) return KV8_EUNSUPPORTED;

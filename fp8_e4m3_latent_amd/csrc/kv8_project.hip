@@ -13,7 +13,7 @@
 //
 // One block = 4 waves computes a 128 x 128 tile of out.  k runs in 8 chunks
 // of 64: each thread loads 32 codes of one row and 32 weights of one column
-// for the next chunk into registers while the current chunk is multiplied;
+// of the chunk three ahead into registers while the current chunk is multiplied;
 // the codes are decoded exactly to bf16 (every e4m3 value is a bf16 value)
 // on their way into LDS.  Operand rows in LDS are 144 bytes (64 bf16 plus 16
 // bytes of padding), so the 16 rows one ds_read_b128 pass serves fall on 16
@@ -71,26 +71,24 @@ __global__ __launch_bounds__(256) void project_rows_kernel(const uint8_t* __rest
     const uint8_t* arow = codes + am * kRowBytes + 32 * lh;
     const uint16_t* wrow = wkv + static_cast<int64_t>(n0 + lr) * kKvLora + 32 * lh;
 
-    u32x4_t ra0, ra1, rw0, rw1, rw2, rw3;
-    auto gload = [&](int kc) {
-        ra0 = *reinterpret_cast<const u32x4_t*>(arow + kPK * kc);
-        ra1 = *reinterpret_cast<const u32x4_t*>(arow + kPK * kc + 16);
-        rw0 = *reinterpret_cast<const u32x4_t*>(wrow + kPK * kc);
-        rw1 = *reinterpret_cast<const u32x4_t*>(wrow + kPK * kc + 8);
-        rw2 = *reinterpret_cast<const u32x4_t*>(wrow + kPK * kc + 16);
-        rw3 = *reinterpret_cast<const u32x4_t*>(wrow + kPK * kc + 24);
+    // three register sets: set kc % 3 holds chunk kc
+    u32x4_t ra[3][2], rw[3][4];
+    auto gload = [&](int kc, int p) {
+        ra[p][0] = *reinterpret_cast<const u32x4_t*>(arow + kPK * kc);
+        ra[p][1] = *reinterpret_cast<const u32x4_t*>(arow + kPK * kc + 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rw[p][i] = *reinterpret_cast<const u32x4_t*>(wrow + kPK * kc + 8 * i);
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int p, int buf) {
         uint8_t* a = &sA[buf][lr * kPRow + 64 * lh];
-        *reinterpret_cast<u32x4_t*>(a) = dec8_bf16(ra0[0], ra0[1]);
-        *reinterpret_cast<u32x4_t*>(a + 16) = dec8_bf16(ra0[2], ra0[3]);
-        *reinterpret_cast<u32x4_t*>(a + 32) = dec8_bf16(ra1[0], ra1[1]);
-        *reinterpret_cast<u32x4_t*>(a + 48) = dec8_bf16(ra1[2], ra1[3]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<u32x4_t*>(a + 32 * i) = dec8_bf16(ra[p][i][0], ra[p][i][1]);
+            *reinterpret_cast<u32x4_t*>(a + 32 * i + 16) = dec8_bf16(ra[p][i][2], ra[p][i][3]);
+        }
         uint8_t* b = &sW[buf][lr * kPRow + 64 * lh];
-        *reinterpret_cast<u32x4_t*>(b) = rw0;
-        *reinterpret_cast<u32x4_t*>(b + 16) = rw1;
-        *reinterpret_cast<u32x4_t*>(b + 32) = rw2;
-        *reinterpret_cast<u32x4_t*>(b + 48) = rw3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(b + 16 * i) = rw[p][i];
     };
 
     const int wm = 64 * (w >> 1), wn = 64 * (w & 1);
@@ -124,34 +122,49 @@ __global__ __launch_bounds__(256) void project_rows_kernel(const uint8_t* __rest
         }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    // chunk kc + 3 is loaded while chunk kc is multiplied and goes into LDS
+    // after chunk kc + 2's products: three product phases for its loads to land
     constexpr int kChunks = kKvLora / kPK;
+    gload(0, 0);
+    gload(1, 1);
+    gload(2, 2);
+    lstore(0, 0);
+    __syncthreads();
 #pragma unroll
     for (int kc = 0; kc < kChunks; ++kc) {
-        if (kc + 1 < kChunks) gload(kc + 1);  // in flight during the products
+        if (kc + 3 < kChunks) gload(kc + 3, kc % 3);  // (set kc % 3 is in LDS already)
         compute(kc & 1);
         // the other buffer was last read before the previous barrier
-        if (kc + 1 < kChunks) lstore((kc + 1) & 1);
+        if (kc + 1 < kChunks) lstore((kc + 1) % 3, (kc + 1) & 1);
         __syncthreads();
     }
 
     // epilogue: register r of accumulator (i, j) is row wm + 32 i + 8 (r / 4) +
-    // 4 g + r % 4 and column wn + 32 j + l32
+    // 4 g + r % 4 and column wn + 32 j + l32.  Each wave's 64 x 64 bf16 tile
+    // goes through LDS (rows of 144 bytes, in the first operand buffers, free
+    // after the last barrier) so that it leaves as 16-byte stores, 8 rows of
+    // 128 bytes per instruction, instead of 2 bytes a lane.
+    uint8_t* const st = &sA[0][0] + w * 64 * kPRow;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (m < n_rows) {
-                const float s = scales[2 * m];
-                uint16_t* o = out + m * N + n0 + wn + l32;
+            const int lrow = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int64_t m = m0 + wm + lrow;
+            const float s = m < n_rows ? scales[2 * m] : 0.0f;
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    o[32 * j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][r] * s));
-            }
+            for (int j = 0; j < 2; ++j)
+                *reinterpret_cast<uint16_t*>(st + lrow * kPRow + 2 * (32 * j + l32)) =
+                    __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][r] * s));
         }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int lrow = 8 * q + (lane >> 3);
+        const int64_t m = m0 + wm + lrow;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + lrow * kPRow + 16 * (lane & 7));
+        if (m < n_rows) *reinterpret_cast<u32x4_t*>(out + m * N + n0 + wn + 8 * (lane & 7)) = v;
     }
 
     // Rc of the block's rows, written by the blocks of the first column tile:

@@ -221,7 +221,7 @@ int kv8_lse_merge(const void* partials, int32_t B, int32_t Q, int32_t H, int32_t
  * w_kv_b         bf16 [N][kv_lora] device array, 16-byte aligned: row n holds
  *                output column n's weights (a linear layer's weight layout).
  * N              output columns, a multiple of 128 (KV8_EUNSUPPORTED otherwise).
- * out            bf16 [n_rows][N]; the products are summed in f32 (bf16 MFMA;
+ * out            bf16 [n_rows][N], 16-byte aligned; the products are summed in f32 (bf16 MFMA;
  *                every e4m3 value is exact in bf16) and the scaled sum is
  *                rounded to nearest even.
  * rope_out       f32 [n_rows][rope], 16-byte aligned, or NULL to skip.

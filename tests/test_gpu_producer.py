@@ -211,3 +211,43 @@ def test_producer_argument_errors(kv8):
         kv8.norm_rope_quantize_rows(xs, ws[:100], 1e-6, ps, 10000.0, codes, scales)
     with pytest.raises(ValueError):
         kv8.norm_rope_quantize_rows(xs, ws, 1e-6, ps[:3], 10000.0, codes, scales)
+
+
+def test_producer_append_then_decode(kv8):
+    """One decode step as the page describes it: the producer normalises, rotates
+    and quantizes each sequence's fresh row into the cache at the sequence's
+    newest position, and the absorbed decode reads the updated cache.  The
+    oracle runs the same two steps; the decode must match it within 1e-3 on the
+    cache the GPU wrote (whose appended codes are checked to the producer's bar
+    against the oracle's first)."""
+    w = workloads.tiny(seed=31, B=4, Q=1, H=128, T=2000, outlier_p=0.0)
+    src = torch.from_numpy(np.ascontiguousarray(w.rows)).cuda()
+    codes = torch.empty((w.n_rows, D), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((w.n_rows, 2), dtype=torch.float32, device="cuda")
+    kv8.quantize_rows(src, codes, scales)
+    g = np.random.default_rng(32)
+    fresh = (g.standard_normal((w.B, D)) * 3.0).astype(np.float32)
+    wt = g.uniform(0.5, 1.5, KL).astype(np.float32)
+    dst = (w.kv_start + w.kv_len - 1).astype(np.int64)
+    pos = (w.kv_len - 1).astype(np.int64)
+    kv8.norm_rope_quantize_rows(torch.from_numpy(fresh).cuda(), torch.from_numpy(wt).cuda(), 1e-6,
+                                torch.from_numpy(pos).cuda(), 10000.0, codes, scales,
+                                dst_rows=torch.from_numpy(dst).cuda())
+    ql = torch.from_numpy(w.q_lat.view(np.int16)).cuda().view(torch.bfloat16)
+    qr = torch.from_numpy(w.q_rope.view(np.int16)).cuda().view(torch.bfloat16)
+    out = kv8.absorb_decode(ql, qr, codes, scales, torch.from_numpy(w.kv_start).cuda(),
+                            torch.from_numpy(w.kv_len).cuda(), w.max_len, w.softmax_scale)
+    torch.cuda.synchronize()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    # the oracle's cache: its quantizer on the rows, its producer on the fresh rows
+    y, oc, os_ = oracle_run(fresh, wt, 1e-6, pos, 10000.0)
+    compare(fresh, y, c[dst], s[dst], oc, os_)
+    rc, rs = oracle.quantize_rows(w.rows)
+    keep = np.setdiff1d(np.arange(w.n_rows), dst)
+    assert np.array_equal(c[keep], rc[keep]) and np.array_equal(s[keep].view(np.uint32), rs[keep].view(np.uint32))
+    ref = oracle.attention(w.q_lat, w.q_rope, c, s, w.kv_start, w.kv_len, Q=w.Q,
+                           softmax_scale=w.softmax_scale)
+    got = out.cpu().numpy().reshape(ref.shape)
+    e = float(np.abs(got - ref).max() / np.abs(ref).max())
+    say("  append + decode: max|d|/max|ref| = %.2e" % e)
+    assert e <= 1e-3

@@ -1172,15 +1172,27 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel
     float lsum = wgt * ml.y;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-    const float wsc = wgt * ml.z;  // weight of split `lane`'s codes
+    const float wsc = wgt * ml.z;  // weight of split `lane`'s codes (0 for an empty split)
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
     const int16_t* po = part_o + br * kKvLora + 8 * lane;
-    for (int s2 = 0; s2 < n_splits; ++s2) {
-        const float w2 = __shfl(wsc, s2, 64);
-        if (w2 != 0.0f) {  // (uniform)
-            const uint4 o8 = *reinterpret_cast<const uint4*>(po + s2 * stride * kKvLora);
-            const float4 v0 = codes4_to_f32(make_uint2(o8.x, o8.y));
-            const float4 v1 = codes4_to_f32(make_uint2(o8.z, o8.w));
+    // eight splits' codes loaded at once, without branches: every split's
+    // codes are written (an empty split's are zeros) and finite, so a zero
+    // weight adds exactly 0; indices past the last split repeat it with
+    // weight 0
+    for (int s2 = 0; s2 < n_splits; s2 += 8) {
+        uint4 o8[8];
+        float w8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int su = s2 + u < n_splits ? s2 + u : n_splits - 1;
+            w8[u] = s2 + u < n_splits ? __shfl(wsc, su, 64) : 0.0f;
+            o8[u] = *reinterpret_cast<const uint4*>(po + static_cast<int64_t>(su) * stride * kKvLora);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w2 = w8[u];
+            const float4 v0 = codes4_to_f32(make_uint2(o8[u].x, o8[u].y));
+            const float4 v1 = codes4_to_f32(make_uint2(o8[u].z, o8[u].w));
             a0.x += w2 * v0.x; a0.y += w2 * v0.y; a0.z += w2 * v0.z; a0.w += w2 * v0.w;
             a1.x += w2 * v1.x; a1.y += w2 * v1.y; a1.z += w2 * v1.z; a1.w += w2 * v1.w;
         }

@@ -345,7 +345,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--legs", default="decode,quantize,splitT,project",
+    ap.add_argument("--legs", default="decode,quantize,splitT,project,ragged",
                     help="comma list of decode, quantize, splitT, project, ragged, copy")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096,
                     help="query rows the oracle times for the CPU baseline (0: skip)")

@@ -104,6 +104,7 @@ namespace {
 
 constexpr int kRowsPerBlock = 128;   // query rows per decode block
 constexpr int kTargetBlocks = 256;   // one block per compute unit
+constexpr int kMaxRange = 4096;      // longest token range of the internal plan
 
 int64_t row_blocks(int32_t Q, int32_t H) {
     return (static_cast<int64_t>(Q) * H + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -177,9 +178,13 @@ int kv8_decode_plan(int32_t B, int32_t Q, int32_t H, int32_t max_len, int32_t* s
                     int32_t* num_splits) {
     if (B < 1 || Q < 1 || H < 1 || max_len < 0 || !split_tokens || !num_splits) return KV8_EINVAL;
     // token ranges of a fixed size (a multiple of the 32-token tile) so that
-    // B x row blocks x ranges fills the compute units
+    // B x row blocks x ranges fills the compute units, and no range is longer
+    // than kMaxRange tokens (with ragged lengths the longest sequences would
+    // otherwise set the time while most blocks have finished)
     const int64_t units = static_cast<int64_t>(B) * row_blocks(Q, H);
     int64_t splits = (kTargetBlocks + units - 1) / units;
+    const int64_t by_cap = (static_cast<int64_t>(max_len) + kMaxRange - 1) / kMaxRange;
+    splits = splits > by_cap ? splits : by_cap;
     const int64_t by_len = (static_cast<int64_t>(max_len) + 1023) / 1024;
     splits = splits < by_len ? splits : by_len;
     if (splits <= 1) {

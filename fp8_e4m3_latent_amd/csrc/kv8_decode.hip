@@ -385,6 +385,46 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int64_t L = load_uniform(p.kv_len + b);
     const int64_t row_base = load_uniform(p.kv_start + b);
 
+    int64_t ts, te;
+    if (p.split_chunk > 0) {
+        ts = static_cast<int64_t>(split) * p.split_chunk;
+        te = ts + p.split_chunk;
+    } else {
+        // equal ranges of ceil(L / n_outer) rows, each cut into n_sub sub-ranges
+        const int n_outer = p.n_splits / p.n_sub;
+        const int outer = split / p.n_sub, sub = split % p.n_sub;
+        const int64_t chunk = (L + n_outer - 1) / n_outer;
+        const int64_t sub_chunk = (chunk + p.n_sub - 1) / p.n_sub;
+        const int64_t o0 = static_cast<int64_t>(outer) * chunk;
+        const int64_t o1 = o0 + chunk;
+        ts = o0 + static_cast<int64_t>(sub) * sub_chunk;
+        te = ts + sub_chunk < o1 ? ts + sub_chunk : o1;
+    }
+    te = L < te ? L : te;
+
+    const int row_hi = (p.QH < row0 + kRowsPerBlock ? p.QH : row0 + kRowsPerBlock) - 1;
+    const int64_t n_first = L - (p.Q - 1) + row0 / p.H;    // visible tokens, first row
+    const int64_t n_last = L - (p.Q - 1) + row_hi / p.H;   // visible tokens, last row
+    te = te < n_last ? te : n_last;
+    const int64_t ntok = te > ts ? te - ts : 0;
+    const int ntiles = static_cast<int>((ntok + kTT - 1) / kTT);
+    const int64_t full_until = te < n_first ? te : n_first;  // no mask below this token
+
+    const int64_t n_row = row_ok ? L - (p.Q - 1) + row / p.H : 0;
+    const int64_t lim_row = n_row < te ? n_row : te;
+
+    // A block whose token range holds no visible token (ranges past a short
+    // sequence's end) writes its rows' (m, l) = (0, 0), which the merge skips,
+    // and stops before any load: its partial codes are never read with a
+    // nonzero weight.
+    if (ntiles == 0 && p.part_o != nullptr) {
+        if (g == 0 && row_ok) {
+            float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 4;
+            *reinterpret_cast<float4*>(ml) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        return;
+    }
+
     // ---- query rows of this wave.  In the MFMA operand order every load
     //      would touch 32 rows (32 bytes of each), so the 32 latent rows
     //      (1 KiB each) are copied whole into LDS first, one row per copy, and
@@ -415,33 +455,6 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         for (int r = 0; r < 4; ++r) qv[32 + r] = qr[4 * g + r];
     }
 
-    int64_t ts, te;
-    if (p.split_chunk > 0) {
-        ts = static_cast<int64_t>(split) * p.split_chunk;
-        te = ts + p.split_chunk;
-    } else {
-        // equal ranges of ceil(L / n_outer) rows, each cut into n_sub sub-ranges
-        const int n_outer = p.n_splits / p.n_sub;
-        const int outer = split / p.n_sub, sub = split % p.n_sub;
-        const int64_t chunk = (L + n_outer - 1) / n_outer;
-        const int64_t sub_chunk = (chunk + p.n_sub - 1) / p.n_sub;
-        const int64_t o0 = static_cast<int64_t>(outer) * chunk;
-        const int64_t o1 = o0 + chunk;
-        ts = o0 + static_cast<int64_t>(sub) * sub_chunk;
-        te = ts + sub_chunk < o1 ? ts + sub_chunk : o1;
-    }
-    te = L < te ? L : te;
-
-    const int row_hi = (p.QH < row0 + kRowsPerBlock ? p.QH : row0 + kRowsPerBlock) - 1;
-    const int64_t n_first = L - (p.Q - 1) + row0 / p.H;    // visible tokens, first row
-    const int64_t n_last = L - (p.Q - 1) + row_hi / p.H;   // visible tokens, last row
-    te = te < n_last ? te : n_last;
-    const int64_t ntok = te > ts ? te - ts : 0;
-    const int ntiles = static_cast<int>((ntok + kTT - 1) / kTT);
-    const int64_t full_until = te < n_first ? te : n_first;  // no mask below this token
-
-    const int64_t n_row = row_ok ? L - (p.Q - 1) + row / p.H : 0;
-    const int64_t lim_row = n_row < te ? n_row : te;
 
     // ---- tile copies.  Wave w issues the 1 KiB copies i = w + 4k of a tile;
     //      the 16 bytes of lane l land at chunk 64 i + l of the raw Lc buffer

@@ -182,7 +182,8 @@ int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope,
  * row with O = 0 has o_scale = 0): 16 bits per value with an absolute error
  * of at most max |O| / 65534 on each.  With x_t = q_lat . xhat_Lc[t] +
  * q_rope . xhat_Rc[t] (before softmax_scale), c = softmax_scale * log2(e);
- * a range with no visible row has l = 0. */
+ * a range with no visible row has m = l = o_scale = 0 and its O codes are
+ * not written (the merge gives such a range weight 0). */
 
 /* Bytes of a partials buffer for these shapes. */
 size_t kv8_partials_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t num_splits);

@@ -51,3 +51,46 @@ def test_argument_errors_are_synchronous():
     assert L.kv8_encode_bits(0, 0, None, None) == 0
     assert L.kv8_encode_bits(5, 1 << 32, 16, None) == -1
     assert L.kv8_decode_codes(None, -3, None, None, None) == -1
+
+
+def test_new_entry_points_reject_bad_arguments_before_any_gpu_work():
+    if not os.path.exists(kv8.LIB_PATH):
+        pytest.skip("libkv8.so not built")
+    L = kv8.lib()
+    f32 = ctypes.c_float
+    # producer: widths, eps, theta, null pointers; zero rows is a no-op
+    nrq = L.kv8_norm_rope_quantize_rows
+    assert nrq(None, 576, 4, 512, 32, None, f32(1e-6), None, f32(1e4), None, None, None, None) == -2
+    assert nrq(None, 576, 4, 512, 64, None, f32(-1.0), None, f32(1e4), None, None, None, None) == -1
+    assert nrq(None, 576, 4, 512, 64, None, f32(float("nan")), None, f32(1e4), None, None, None, None) == -1
+    assert nrq(None, 576, 4, 512, 64, None, f32(1e-6), None, f32(0.0), None, None, None, None) == -1
+    assert nrq(None, 576, 4, 512, 64, None, f32(1e-6), None, f32(1e4), None, None, None, None) == -1
+    assert nrq(None, 576, 0, 512, 64, None, f32(1e-6), None, f32(1e4), None, None, None, None) == 0
+    # projection: N must be a multiple of 128; null pointers; empty shapes
+    pr = L.kv8_project_rows
+    assert pr(None, None, 4, 512, 64, None, 100, None, None, None) == -2
+    assert pr(None, None, 4, 512, 64, None, 128, None, None, None) == -1
+    assert pr(None, None, 0, 512, 64, None, 128, None, None, None) == 0
+    assert pr(None, None, -1, 512, 64, None, 128, None, None, None) == -1
+
+
+def test_decode_plan():
+    """The internal split plan (host arithmetic only): ranges fill 256 compute
+    units, no range is longer than 4,096 tokens and none shorter than 1,024
+    unless the sequence is."""
+    if not os.path.exists(kv8.LIB_PATH):
+        pytest.skip("libkv8.so not built")
+    # B=32, H=128, T=8192: 32 row blocks -> 8 ranges of 1,024 tokens
+    assert kv8.decode_plan(32, 1, 128, 8192) == (1024, 8)
+    # one short sequence: no split
+    assert kv8.decode_plan(1, 1, 16, 1024) == (1024, 1)
+    # 256k tokens, one sequence: 256 ranges of 1,024
+    assert kv8.decode_plan(1, 1, 128, 262144) == (1024, 256)
+    # ragged B=64, Q=4: 256 row blocks already fill the GPU; the 4,096-token
+    # cap cuts the longest (65,536) into 16 ranges
+    assert kv8.decode_plan(64, 4, 128, 65536) == (4096, 16)
+    for B, Q, H, T in ((3, 1, 16, 777), (8, 2, 64, 50000), (200, 1, 128, 3000), (1, 1, 128, 1)):
+        k, n = kv8.decode_plan(B, Q, H, T)
+        assert k % 32 == 0 or n == 1
+        assert n * k >= T and (n - 1) * k < T
+        assert n == 1 or k <= 4096

@@ -14,7 +14,9 @@ latent rows of 512 Lc + 64 Rc e4m3 codes with per-row f32 scales.  Each step
 Three copies of the cache (3 x 153 MB, more than the 256 MB last-level cache)
 are used in rotation so every step reads its KV from HBM.  Inputs are resident
 in HBM before the timed region; times come from HIP events on the stream the
-kernels run on.  The default 400 untimed steps (about 50 ms) bring the GPU to
+kernels run on.  The timed steps have nothing between their kernels; a
+separate pass over the same number of steps, with events between the
+kernels, gives the per-kernel breakdown (`kernel_ms`).  The default 400 untimed steps (about 50 ms) bring the GPU to
 its working clock first: with a handful of warmup steps the timed steps ran
 about 15% slower.  The decode kernel's roofline uses its duration over launches
 of that kernel alone, back to back on the same rotating caches (the per-step
@@ -129,17 +131,22 @@ def leg_decode(torch, kv8, W, steps, warmup, cpu_sample_rows):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # per-kernel breakdown: the same steps with HIP events between the kernels
     timer = Timer(torch, 4, steps)
+    for t in range(steps):
+        step(warmup + t, timer, t)
+    torch.cuda.synchronize()
+    iv = timer.intervals_ms()                 # [steps, 3]: append, decode, merge
+    # the timed steps: nothing but the steps' kernels between the two events
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for t in range(steps):
-        step(warmup + t, timer, t)
+        step(warmup + steps + t)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    iv = timer.intervals_ms()                 # [steps, 3]: append, decode, merge
     ms_step = total_ms / steps
     flops = float(FLOPS_PER_ROW_TOKEN) * B * Q * H * T
     kv_bytes = float(KV_BYTES_PER_TOKEN) * B * T
@@ -164,7 +171,7 @@ def leg_decode(torch, kv8, W, steps, warmup, cpu_sample_rows):
     torch.cuda.synchronize()
     e0.record()
     for i in range(b2b):
-        c = (warmup + steps + i) % n_copies
+        c = (warmup + 2 * steps + i) % n_copies
         kv8.absorb_decode_partials(qs[c][0], qs[c][1], caches[c][0], caches[c][1], kv_start, kv_len,
                                    T, sc, split_tokens, n_splits, partials)
     e1.record()

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void project_rows_kernel(const uint8_t* __rest
                                                            float* __restrict__ rope_out) {
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][kPTile];
     __shared__ __attribute__((aligned(16))) uint8_t sW[2][kPTile];
+    __shared__ float s_rs[kPM];  // Lc scales of the block's rows
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -125,6 +126,9 @@ __global__ __launch_bounds__(256) void project_rows_kernel(const uint8_t* __rest
     // chunk kc + 3 is loaded while chunk kc is multiplied and goes into LDS
     // after chunk kc + 2's products: three product phases for its loads to land
     constexpr int kChunks = kKvLora / kPK;
+    // the row scales go to LDS at the start, so that the epilogue does not
+    // wait for their loads
+    if (tid < kPM) s_rs[tid] = m0 + tid < n_rows ? scales[2 * (m0 + tid)] : 0.0f;
     gload(0, 0);
     gload(1, 1);
     gload(2, 2);
@@ -150,8 +154,7 @@ __global__ __launch_bounds__(256) void project_rows_kernel(const uint8_t* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int lrow = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-            const int64_t m = m0 + wm + lrow;
-            const float s = m < n_rows ? scales[2 * m] : 0.0f;
+            const float s = s_rs[wm + lrow];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 *reinterpret_cast<uint16_t*>(st + lrow * kPRow + 2 * (32 * j + l32)) =

@@ -79,7 +79,6 @@ constexpr int kRawLcBytes = kTT * kKvLora;       // 16384: raw Lc codes of a til
 constexpr int kRawRcBytes = kTT * kRope;         // 2048: raw Rc codes of a tile
 constexpr int kLcStride = 2 * kKvLora + 64;      // 1088: fp16 Lc row + padding
 constexpr int kLcBytes = kTT * kLcStride;        // 34816
-constexpr int kDmaPerTile = (kRawLcBytes + kRawRcBytes) / 1024;  // 18 wave-wide 1 KiB copies
 
 constexpr int kScoreAhead = 3;                   // score operand loads in flight
 constexpr int kCtxAhead = 3;                     // context operand loads in flight
@@ -159,12 +158,6 @@ __device__ __forceinline__ void barrier_after_copies<5>() {
 // is a wave-uniform base (SGPR pair) plus a 32-bit per-lane byte offset.
 __device__ __forceinline__ void copy_to_lds_b128(const void* base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void copy_to_lds_b32(const void* base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");

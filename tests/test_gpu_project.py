@@ -114,3 +114,36 @@ def test_project_argument_errors(kv8):
         kv8.project_rows(codes, scales, wb)
     with pytest.raises(ValueError):
         kv8.project_rows(codes, scales[:3], weights(128, 57)[0])
+
+
+def test_project_degenerate_rows_and_empty(kv8):
+    """Rows the quantizer treats specially: all zero (both scales 0), zero Lc or
+    zero Rc only, a subnormal amax (stored as scale 0), Lc scaled by 1e30 and
+    by 1e-30, a NaN element (stored as code 0) and a constant row at the e4m3
+    maximum.  Zero-scale parts must project to exact zeros; n = 0 is a no-op."""
+    x = np.random.default_rng(60).standard_normal((8, D)).astype(np.float32)
+    x[0] = 0.0
+    x[1, :KL] = 0.0
+    x[2, KL:] = 0.0
+    x[3] = np.float32(1e-40) * np.sign(x[3])
+    x[4, :KL] *= np.float32(1e30)
+    x[5, 10] = np.nan
+    x[6, :KL] = 448.0
+    x[7, :KL] *= np.float32(1e-30)
+    codes = torch.empty((8, D), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((8, 2), dtype=torch.float32, device="cuda")
+    kv8.quantize_rows(torch.from_numpy(x).cuda(), codes, scales)
+    wb, wbits = weights(256, 61)
+    out, rope = kv8.project_rows(codes, scales, wb)
+    torch.cuda.synchronize()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    rc, rs = oracle.quantize_rows(x)
+    assert np.array_equal(c, rc) and np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    check(c, s, wbits, np.arange(8), out, rope)
+    o = out.float().cpu().numpy()
+    assert not np.any(np.isnan(o))
+    assert np.all(o[[0, 1, 3]] == 0.0)
+    assert np.all(rope.cpu().numpy()[[0, 2, 3]] == 0.0)
+    e_out, e_rope = kv8.project_rows(codes[:0], scales[:0], wb)
+    torch.cuda.synchronize()
+    assert tuple(e_out.shape) == (0, 256) and tuple(e_rope.shape) == (0, 64)

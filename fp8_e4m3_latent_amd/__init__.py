@@ -73,9 +73,9 @@ def lib():
     L.kv8_absorb_decode_partials.restype = ctypes.c_int
     L.kv8_absorb_decode_partials.argtypes = dec[:-1] + [i32, i32, vp, sz, vp]
     L.kv8_lse_merge.restype = ctypes.c_int
-    L.kv8_lse_merge.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, vp]
+    L.kv8_lse_merge.argtypes = [vp, sz, i32, i32, i32, i32, i32, f32, vp, vp]
     L.kv8_encode_bits.restype = ctypes.c_int
-    L.kv8_encode_bits.argtypes = [u32, u64, vp, vp]
+    L.kv8_encode_bits.argtypes = [u32, u64, i32, vp, vp]
     L.kv8_decode_codes.restype = ctypes.c_int
     L.kv8_decode_codes.argtypes = [vp, i64, vp, vp, vp]
     _lib = L
@@ -287,18 +287,20 @@ def lse_merge(partials, B, Q, H, num_splits, softmax_scale, out=None, stream=Non
     if out is None:
         out = torch.empty((B, Q, H, KV_LORA), dtype=torch.float32, device=partials.device)
     po = _check(out, "out", torch.float32, 4)
-    _call("kv8_lse_merge", pp, B, Q, H, KV_LORA, int(num_splits), ctypes.c_float(softmax_scale),
-          po, _stream(stream))
+    _call("kv8_lse_merge", pp, partials.numel() * 4, B, Q, H, KV_LORA, int(num_splits),
+          ctypes.c_float(softmax_scale), po, _stream(stream))
     return out
 
 
-def encode_bits(first, count, out, stream=None):
-    """out[k] = device encoder's code of the f32 with bit pattern first + k."""
+def encode_bits(first, count, out, encoder=0, stream=None):
+    """out[k] = device code of the f32 with bit pattern first + k, from the
+    quantizer's encoder (0) or the integer bit-math encoder (1)."""
     torch = _torch()
     po = _check(out, "out", torch.uint8, 1)
     if out.numel() < count:
         raise ValueError("out too small")
-    _call("kv8_encode_bits", ctypes.c_uint32(first), ctypes.c_uint64(count), po, _stream(stream))
+    _call("kv8_encode_bits", ctypes.c_uint32(first), ctypes.c_uint64(count), int(encoder), po,
+          _stream(stream))
 
 
 def decode_codes(codes, stream=None):

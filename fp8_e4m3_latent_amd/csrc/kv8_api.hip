@@ -79,11 +79,12 @@ int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, 
                                              static_cast<hipStream_t>(stream)));
 }
 
-int kv8_encode_bits(uint32_t first, uint64_t count, uint8_t* out, void* stream) {
+int kv8_encode_bits(uint32_t first, uint64_t count, int32_t encoder, uint8_t* out, void* stream) {
+    if (encoder != 0 && encoder != 1) return KV8_EINVAL;
     if (count == 0) return KV8_OK;
     if (!out || !aligned(out, 4)) return KV8_EINVAL;
     if (count > (uint64_t(1) << 32) - first) return KV8_EINVAL;
-    return launched(kv8::launch_encode_bits(first, count, out, static_cast<hipStream_t>(stream)));
+    return launched(kv8::launch_encode_bits(first, count, encoder, out, static_cast<hipStream_t>(stream)));
 }
 
 int kv8_decode_codes(const uint8_t* codes, int64_t n, uint16_t* out_bf16, uint16_t* out_f16,
@@ -214,6 +215,9 @@ int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
                           kv_lora, rope, softmax_scale, static_cast<float*>(partials) /* no out */);
     if (rc != KV8_OK) return rc;
     if (num_splits < 1 || num_splits > (1 << 20) || split_tokens < 0) return KV8_EINVAL;
+    // fixed-size ranges must cover every row a sequence may hold
+    if (split_tokens > 0 && static_cast<int64_t>(split_tokens) * num_splits < max_len)
+        return KV8_EINVAL;
     if (!partials || !aligned(partials, 256) ||
         partials_bytes < kv8::splitT_workspace_bytes(B, Q, H, num_splits))
         return KV8_EWORKSPACE;
@@ -226,11 +230,14 @@ int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
     return launched(kv8::launch_absorb_decode(d, static_cast<hipStream_t>(stream), false));
 }
 
-int kv8_lse_merge(const void* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
-                  int32_t num_splits, float softmax_scale, float* out, void* stream) {
-    if (B < 1 || Q < 1 || H < 1 || num_splits < 1) return KV8_EINVAL;
+int kv8_lse_merge(const void* partials, size_t partials_bytes, int32_t B, int32_t Q, int32_t H,
+                  int32_t kv_lora, int32_t num_splits, float softmax_scale, float* out,
+                  void* stream) {
+    if (B < 1 || Q < 1 || H < 1 || num_splits < 1 || num_splits > (1 << 20)) return KV8_EINVAL;
     if (kv_lora != kv8::kKvLora) return KV8_EUNSUPPORTED;
     if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16)) return KV8_EINVAL;
+    if (static_cast<int64_t>(Q) * H > (int64_t(1) << 21)) return KV8_EUNSUPPORTED;
+    if (partials_bytes < kv8::splitT_workspace_bytes(B, Q, H, num_splits)) return KV8_EWORKSPACE;
     if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
         softmax_scale == -INFINITY)
         return KV8_EINVAL;

@@ -99,7 +99,7 @@ struct DecodeArgs {
     float c;           // softmax_scale * log2(e)
     float* out;        // [B][QH][512] when no partials are written
     int16_t* part_o;   // [n_splits][B][QH][512] codes, O = code * o_scale
-    float* part_ml;    // [n_splits][B][QH][4]: reference score m, sum l, o_scale, 0
+    float* part_ml;    // [n_splits][B][QH] RangeStat records (16 bytes each)
 };
 
 // s_waitcnt with only the vector-memory counter limited (lgkm and exp free)
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     __shared__ __attribute__((aligned(16))) uint8_t s_lc[kNBuf][kLcBytes];
     __shared__ __attribute__((aligned(16))) float s_sc[kNBuf][2 * kTT];   // copied (Lc, Rc) scales
     __shared__ __attribute__((aligned(16))) float s_scd[kNBuf][3 * kTT];  // s_Lc, s_Rc, s_Lc / 2^e
-    __shared__ uint32_t s_red[kWaves];
-    __shared__ int s_restart;
+    __shared__ uint32_t s_red[3][kWaves];
+    __shared__ int s_restart, s_shift;
     // per-row output factors of the epilogue, in the first raw Lc buffer (no
     // tile copy or decode is in flight by then)
     float (*const s_row)[32] = reinterpret_cast<float (*)[32]>(&s_raw[0][0]);
@@ -403,15 +403,21 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int ntiles = static_cast<int>((ntok + kTT - 1) / kTT);
     const int64_t full_until = te < n_first ? te : n_first;  // no mask below this token
 
-    const int64_t n_row = row_ok ? L - (p.Q - 1) + row / p.H : 0;
-    const int64_t lim_row = n_row < te ? n_row : te;
+    // visible tokens of this lane's row in the range, relative to ts (rebuilt
+    // where a tile needs masking, so that it is not kept live across the loop)
+    auto row_limit_rel = [&]() {
+        const int r = row0 + 32 * w + (fresh_lane_id() & 31);
+        const int64_t n_row = r < p.QH ? L - (p.Q - 1) + r / p.H : 0;
+        const int64_t lim = n_row < te ? n_row : te;
+        return static_cast<int>(lim - ts);
+    };
 
     // A block whose token range holds no visible token (ranges past a short
     // sequence's end) writes its rows' (m, l) = (0, 0), which the merge skips,
     // and stops before any load: its partial codes are never read with a
     // nonzero weight.
     if (ntiles == 0 && p.part_o != nullptr) {
-        if (g == 0 && row_ok) {
+        if (g == 0 && row_ok) {  // (m = +0.0 as f64, l = 0, o_scale = 0)
             float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 4;
             *reinterpret_cast<float4*>(ml) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
@@ -501,16 +507,24 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // buffers that stage the queries)
     if (ntiles > 0) issue_tile(0);
 
-    // ---- 2^e above the largest Lc scale of the token range
-    uint32_t rbits = 0;
+    // ---- the range's largest Lc scale, largest Rc scale and smallest Lc
+    //      scale (bit patterns of non-negative floats order as integers)
+    uint32_t lbits = 0, rbits = 0, nbits = 0xFFFFFFFFu;
     for (int64_t t0 = ts + tid; t0 < te; t0 += 4 * kThreads) {  // four loads in flight
-        uint32_t v[4];
+        uint2 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t t = t0 + u * kThreads;
-            v[u] = t < te ? __float_as_uint(p.scales[2 * (row_base + t)]) : 0u;
+            v[u] = t < te ? *reinterpret_cast<const uint2*>(p.scales + 2 * (row_base + t))
+                          : make_uint2(0u, 0u);
         }
-        rbits = max(rbits, max(max(v[0], v[1]), max(v[2], v[3])));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool in = t0 + u * kThreads < te;
+            lbits = max(lbits, v[u].x);
+            rbits = max(rbits, v[u].y);
+            nbits = in ? min(nbits, v[u].x) : nbits;
+        }
     }
 
     // ---- query row l32 of this wave: B operand of the score MFMA, fp16 after
@@ -539,16 +553,40 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         }
     }
 
+    lbits = wave_max_u32(lbits);
     rbits = wave_max_u32(rbits);
-    if (lane == 0) s_red[w] = rbits;
-    __syncthreads();  // (also: every wave has read its staged queries)
-    rbits = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
-    int e = 0;
-    if (rbits != 0) {
-        e = static_cast<int>((rbits >> 23) & 0xFF) - 126;  // r < 2^e
-        e = e < -126 ? -126 : e;
+    nbits = ~wave_max_u32(~nbits);
+    if (lane == 0) {
+        s_red[0][w] = lbits;
+        s_red[1][w] = rbits;
+        s_red[2][w] = nbits;
     }
-    e = __builtin_amdgcn_readfirstlane(e);
+    __syncthreads();  // (also: every wave has read its staged queries)
+    lbits = max(max(s_red[0][0], s_red[0][1]), max(s_red[0][2], s_red[0][3]));
+    rbits = max(max(s_red[1][0], s_red[1][1]), max(s_red[1][2], s_red[1][3]));
+    nbits = min(min(s_red[2][0], s_red[2][1]), min(s_red[2][2], s_red[2][3]));
+    // 2^e just above the largest Lc scale (normalises the probabilities of
+    // the context pass) and 2^ex just above the largest scale of either
+    // segment (normalises the scores: s / 2^ex < 1 keeps every score below
+    // 2^32 in accumulator units, whatever the magnitude of the rows)
+    auto exp_above = [](uint32_t bits) {
+        int k = 0;
+        if (bits != 0) {
+            k = static_cast<int>((bits >> 23) & 0xFF) - 126;  // value < 2^k
+            k = k < -126 ? -126 : k;
+        }
+        return k;
+    };
+    const int e = __builtin_amdgcn_readfirstlane(exp_above(lbits));
+    const int ex = __builtin_amdgcn_readfirstlane(exp_above(max(lbits, rbits)));
+    // The probabilities of a row lose fp16 precision only when the tokens that
+    // carry its weight have Lc scales far below the range's largest.  A range
+    // whose smallest Lc scale (zero included) is more than 2^6 below its
+    // largest is run "watched": the first pass records each row's largest
+    // probability operand, and a row where it is small gets its operands
+    // shifted up by a power of two in a second pass.
+    const bool watched = nbits != 0xFFFFFFFFu && lbits != 0 &&
+                         __uint_as_float(nbits) * 64.0f < __uint_as_float(lbits);
 
     // tiles 1 and 2 go to buffers that staged the queries; the conversion
     // below (pinned after them) runs while they are in flight
@@ -568,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int sc_base0 = l32 * kLcStride + 16 * (g ^ hsw);        // ks even (+64 (ks >> 1))
     const int sc_base1 = l32 * kLcStride + 16 * ((2 + g) ^ hsw);  // ks odd
     // score A operand, Rc: token l32, chunks 2 g and 2 g + 1
-    const int rope_off = 16 * (64 * g + l32);
+    // (token l32, chunks 2 g and 2 g + 1: byte 16 lane of the raw Rc layout)
     // context B operand: lane (G = lane / 16, gi = lane % 16) of k-group g
     // takes token 4 g + 8 h + gi / 4 (+ 16 kc) at dims 32 dt + 16 (G % 2) +
     // 4 (gi % 4) for its transpose load h
@@ -586,21 +624,25 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int d_hs = (d_t >> 2) & 3;
     const int d_wA = d_t * kLcStride + 16 * ((2 * d_s) ^ d_hs);  // + 256 j; odd chunk: ^ 16
 
-    // Scores x are kept in accumulator units times sgn = sign(c) (the row
-    // scales carry the sign), so that with c_row = |softmax_scale log2(e)| 2^kq
-    // the weights are p = 2^(c_row (x - m_x)) with m_x the row's largest x: the
-    // difference is taken first, so the reference token gets exactly 1 at any
-    // score magnitude.  (c_row is clamped to the finite normal range so that
-    // c_row (x - m_x) is 0 at the reference and -inf at masked tokens, never
-    // NaN.)
+    // Scores x are kept in accumulator units times sgn = sign(c) / 2^ex (the
+    // row scales carry the sign and are divided by 2^ex, so |x| < 2^32 for
+    // rows of any finite magnitude), so that with c_row = |softmax_scale
+    // log2(e)| 2^(kq + ex) the weights are p = 2^(c_row (x - m_x) + dsh) with
+    // m_x the row's largest x: the difference is taken first, so the reference
+    // token gets exactly 2^dsh at any score magnitude.  dsh is 0 unless the
+    // row's probability operands were found too small for fp16 (watched
+    // ranges); the sum l carries the same 2^dsh, so O / l does not change.
+    // (c_row is clamped to the finite normal range so that c_row (x - m_x) is
+    // 0 at the reference and -inf at masked tokens, never NaN.)
     const float sgn = p.c >= 0.0f ? 1.0f : -1.0f;  // (uniform)
-    float c_row = __builtin_ldexpf(fabsf(p.c), kq);
+    float c_row = __builtin_ldexpf(fabsf(p.c), kq + ex);
     if (!(c_row <= FLT_MAX)) c_row = FLT_MAX;
     if (c_row < FLT_MIN) c_row = FLT_MIN;
     const float mask_val = -INFINITY;  // masked x, and "no reference yet"
     float m_x = mask_val;
     float l_run = 0.0f;        // this lane's half of the row sum
-    const int lim_rel0 = static_cast<int>(lim_row - ts);  // visible tokens of the row in the range
+    float dsh = 0.0f;          // log2 of the row's operand shift (integer)
+    float pmax = 0.0f;         // largest probability operand of the lane in this pass
 
     f32x16_t O[16];
 #pragma unroll
@@ -619,13 +661,14 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         const uint4 v = half == 0 ? dec8_f16(r.x, r.y) : dec8_f16(r.z, r.w);
         *reinterpret_cast<uint4*>(lc + (half == 0 ? d_wA : (d_wA ^ 16)) + 256 * j) = v;
     };
-    // (every wave writes the same values: lane t < 32 the signed s_Lc, s_Rc
-    // of token t, lane 32 + t the value s_Lc / 2^e of token t, twice)
+    // (every wave writes the same values: lane t < 32 the signed s_Lc / 2^ex,
+    // s_Rc / 2^ex of token t, lane 32 + t the value s_Lc / 2^e of token t,
+    // twice)
     auto decode_scales = [&](int buf) {
         const float2 sc = *reinterpret_cast<const float2*>(&s_sc[buf][2 * l32]);
         float* d = &s_scd[buf][0];
-        const float v0 = g == 0 ? sgn * sc.x : __builtin_ldexpf(sc.x, -e);
-        const float v1 = g == 0 ? sgn * sc.y : v0;
+        const float v0 = __builtin_ldexpf(g == 0 ? sgn * sc.x : sc.x, g == 0 ? -ex : -e);
+        const float v1 = g == 0 ? __builtin_ldexpf(sgn * sc.y, -ex) : v0;
         d[g == 0 ? l32 : 2 * kTT + l32] = v0;
         d[g == 0 ? kTT + l32 : 2 * kTT + l32] = v1;
     };
@@ -656,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     };
     auto mask_x = [&](int tile) {
         if (ts + static_cast<int64_t>(tile) * kTT + kTT > full_until) {  // (uniform)
-            const int rel = lim_rel0 - tile * kTT - 4 * g;
+            const int rel = row_limit_rel() - tile * kTT - 4 * g;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int t = 8 * (j >> 2) + (j & 3);
@@ -674,6 +717,8 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     f16x8_t ropeop;
     auto rope_load = [&](int tile) {
         const uint8_t* rc = &s_rc[tile & (kRcBufs - 1)][0];
+        const int ln = fresh_lane_id();
+        const int rope_off = 16 * (ln + (ln & 32));  // (= 16 (64 g + l32))
         rope[0] = lds_load<uint4>(rc, rope_off);
         rope[1] = lds_load<uint4>(rc, rope_off + 16 * 32);
     };
@@ -715,10 +760,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //          of the lane's 16 scores
     //   11     the row maximum (with the other half of the wave)
     //   12     reference update
-    //   13-20  p = 2^(c_row (x - ref)) for tokens 2 (k - 13) and 2 (k - 13) + 1
+    //   13-20  p = 2^(c_row (x - ref) + dsh) for tokens 2 (k - 13) and
+    //          2 (k - 13) + 1
     //   21-24  lsum = sum of the p (pairwise), loads of s_Lc / 2^e for token
     //          group k - 21
-    //   25-28  P' = p s_Lc / 2^e for token group k - 25
+    //   25-28  P' = p s_Lc / 2^e for token group k - 25, and the lane's largest
+    //          P' of the real tiles
     //   29-30  P' packed to fp16 as the A operand of context k-step k - 29
     constexpr int kSoftSteps = 31;
     uint4 pa[2], pn[2];  // P' of the tile in the context MFMAs, and of the next
@@ -765,8 +812,8 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         } else if (k < 16) {
             const int j = 2 * (k - 8);
             pin(x[j]); pin(x[j + 1]);
-            x[j] = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
-            x[j + 1] = __builtin_amdgcn_exp2f(c_row * (x[j + 1] - ref));
+            x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(c_row, x[j] - ref, dsh));
+            x[j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(c_row, x[j + 1] - ref, dsh));
             pin(x[j]); pin(x[j + 1]);
         } else if (k < 18) {
             scales_load_e(buf, k - 16);
@@ -792,6 +839,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             x[4 * q4 + 1] *= se4[q4].y;
             x[4 * q4 + 2] *= se4[q4].z;
             x[4 * q4 + 3] *= se4[q4].w;
+            {
+                const float t = max3(max3(pmax, x[4 * q4], x[4 * q4 + 1]), x[4 * q4 + 2], x[4 * q4 + 3]);
+                pmax = real ? t : pmax;
+            }
             pin(x[4 * q4]); pin(x[4 * q4 + 1]); pin(x[4 * q4 + 2]); pin(x[4 * q4 + 3]);
         } else {
             const int kc = k - 24;
@@ -818,13 +869,15 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bv);
     };
 
-    if (tid == 0) s_restart = 0;
+    if (tid == 0) {
+        s_restart = 0;
+        s_shift = 0;
+    }
 
-    // At most two passes over the token range: a row whose later tile exceeds
-    // its reference maximum by more than kLazyLog2 raises the reference and
-    // flags the block; the pass still finishes (so every reference ends within
-    // kLazyLog2 of every tile maximum) and the range is then run once more
-    // from a zero accumulator.
+    // A row whose later tile exceeds its reference maximum by more than
+    // kLazyLog2 raises the reference and flags the block; the pass still
+    // finishes (so every reference ends within kLazyLog2 of every tile
+    // maximum) and the range is then run once more from a zero accumulator.
     //
     // Software pipeline (tile i): copy(i) is issued four tiles ahead and
     // waited for at the end of the next iteration, decode(i) runs two tiles
@@ -842,15 +895,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         if (w == 2) barrier_after_copies<4>();
         else barrier_after_copies<5>();
     };
-    for (int attempt = 0; attempt < 2; ++attempt) {
+    // One pass over the token range (every pass also records each lane's
+    // largest probability operand, which only a watched pass reads).
+    auto run_pass = [&]() {
         if (ntiles > 0) {
-            if (attempt > 0) {
-                issue_tile(0);
-                wait_all_copies();
-                __syncthreads();
-                issue_tile(1);
-                issue_tile(2);
-            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 decode_load(0, j);
@@ -928,18 +976,63 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             if (it0 + 1 < ntiles) iteration(it0 + 1, std::integral_constant<int, 1>{});
             if (it0 + 2 < ntiles) iteration(it0 + 2, std::integral_constant<int, 2>{});
         }
+    };
+
+    // At most three passes.  A pass in which some row raised its reference
+    // is run again (the references are then final); a watched pass without a
+    // raise then gives every row whose largest probability operand P' is
+    // below 2^-6 the shift 2^dsh that brings it to [1, 2) (at most 2^100, and
+    // with l 2^dsh below 2^120), and one more pass runs with those shifts.
+    bool track = __builtin_amdgcn_readfirstlane(watched ? 1 : 0) != 0;
+    for (int attempt = 0; attempt < 3; ++attempt) {
+        if (attempt > 0 && ntiles > 0) {
+            issue_tile(0);
+            wait_all_copies();
+            __syncthreads();
+            issue_tile(1);
+            issue_tile(2);
+        }
+        run_pass();
         if (restart) s_restart = 1;
         __syncthreads();
-        if (!s_restart) break;
+        const bool any_raise = s_restart != 0;
+        if (track && !any_raise) {
+            const float pr = fmaxf(pmax, other_half(pmax));  // the row's largest P'
+            const float lt = pair_sum(l_run);
+            if (lt > 0.0f && pr > 0.0f && pr < 0x1p-6f) {
+                int pe, le;
+                (void)frexpf(pr, &pe);  // pr in [2^(pe-1), 2^pe)
+                (void)frexpf(lt, &le);
+                int d = 1 - pe;
+                d = d < 100 ? d : 100;
+                d = d < 120 - le ? d : 120 - le;
+                if (d > 0) {
+                    dsh = static_cast<float>(d);
+                    s_shift = 1;
+                }
+            }
+        }
         __syncthreads();
-        if (tid == 0) s_restart = 0;
+        const bool any_shift = s_shift != 0;
+        if (!any_raise && !any_shift) break;
+        __syncthreads();  // (every wave has read the flags)
+        if (tid == 0) {
+            s_restart = 0;
+            s_shift = 0;
+        }
+        track = any_raise && track;
         restart = false;
         wait_vmcnt<0>();  // the last re-copies land before the buffers are reused
 #pragma unroll
         for (int dt = 0; dt < 16; ++dt) zero_acc(O[dt]);
         l_run = 0.0f;
+        pmax = 0.0f;
     }
-    wait_vmcnt<0>();  // no tile copy may land after the block has finished
+    // No tile copy may land after this point: the epilogue reuses the first
+    // raw buffer, which the last iteration's (clamped) re-copies of other
+    // waves may still be writing, so every wave waits for its own copies and
+    // then for the others at the barrier.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
     // ---------------- epilogue: rows of O register j are 8(j/4) + 4g + j%4
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -952,8 +1045,9 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int el = fresh_lane_id();
     const int e32 = el & 31, eg = el >> 5;
     if (p.part_o == nullptr) {
-        // the probabilities carried 2^-e: out = 2^e O / l
-        if (eg == 0) s_row[w][e32] = l_tot > 0.0f ? __builtin_ldexpf(1.0f / l_tot, e) : 0.0f;
+        // the probabilities carried 2^-e: out = 2^e (O / l), with the shift
+        // 2^dsh in both O and l (2^e / l alone could leave the float range)
+        if (eg == 0) s_row[w][e32] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         __builtin_amdgcn_wave_barrier();
         float* dst = p.out + static_cast<int64_t>(b) * p.QH * kKvLora;
 #pragma unroll
@@ -969,7 +1063,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                     for (int dt = 0; dt < 16; ++dt) {
                         float v;
                         asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(O[dt][4 * q4 + r]));
-                        o[32 * dt] = v * fv[r];
+                        o[32 * dt] = __builtin_ldexpf(v * fv[r], e);
                     }
                 }
             }
@@ -977,9 +1071,11 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         return;
     }
 
-    // Partial O as 16-bit codes, one scale per row: code = round(32767 O /
-    // max_row |O|) (clamped to [-32767, 32767]), O = code * o_scale with
-    // o_scale = 2^e max_row |O| / 32767 in true units.  |O| is compared as
+    // Partial O / l as 16-bit codes, one scale per row: code = round(32767 O /
+    // max_row |O|) (clamped to [-32767, 32767]), O / l = code * o_scale with
+    // o_scale = 2^e max_row |O| / (32767 l) in true units (the normalised
+    // context of the range, which stays within the range of its rows'
+    // values, so it is finite for every finite cache).  |O| is compared as
     // the bit pattern of a non-negative float; the row maximum of register j
     // (row 8 (j / 4) + 4 g + j % 4, columns 32 dt + l32) combines the 16
     // registers of the lane and then the 32 lanes of its half.
@@ -1037,19 +1133,33 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     if (eg == 0 && row_ok) {
         float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 4;
         const float rmax = s_row[w][e32];
+        const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        // reference score in true units (f64: scores of large rows and large
+        // queries leave the f32 range), the unshifted sum, the code scale
+        const double m_true = __builtin_ldexp(static_cast<double>(sgn * m_x), kq + ex);
+        const uint64_t mb = __builtin_bit_cast(uint64_t, m_true);
         *reinterpret_cast<float4*>(ml) =
-            make_float4(__builtin_ldexpf(sgn * m_x, kq),  // reference score in true units
-                        l_tot, __builtin_ldexpf(rmax * (1.0f / 32767.0f), e), 0.0f);
+            make_float4(__uint_as_float(static_cast<uint32_t>(mb)), __uint_as_float(static_cast<uint32_t>(mb >> 32)),
+                        __builtin_ldexpf(l_tot, -static_cast<int>(dsh)),
+                        __builtin_ldexpf(rmax * inv_l * (1.0f / 32767.0f), e));
     }
 }
 
-// out[b, row, :] = sum_s w_s O_s / sum_s w_s l_s over the splits with
-// l_s > 0, w_s = 2^(c (m_s - m*)) with m* the reference of largest c m_s;
-// zero when no split saw a token.
+// The per-range statistics of a partial row: the reference score m in true
+// units (f64), the sum l = sum_t 2^(c (x_t - m)), and the scale of the 16-bit
+// codes of the range's normalised context O / l.
+struct RangeStat {
+    double m;
+    float l;
+    float o_scale;
+};
+static_assert(sizeof(RangeStat) == 16, "partial statistics record");
+
+// out[b, row, :] = sum_s (w_s l_s / L) (O_s / l_s) over the ranges with
+// l_s > 0, w_s = 2^(c (m_s - m*)) with m* the reference of largest c m_s and
+// L = sum_s w_s l_s; zero when no range saw a token.  The weights are formed
+// before they meet the codes, so no intermediate leaves the float range.
 //
-// Block = 256 threads = one (b, row) and one quarter (128 columns) of the
-// output row: 8 groups of 32 lanes, group g summing the splits s = g mod 8
-// (lane = 4 columns), then one reduction over the groups in LDS.
 // four 16-bit codes (two dwords, low half first) as floats
 __device__ __forceinline__ float4 codes4_to_f32(uint2 c) {
     return make_float4(static_cast<float>(static_cast<int16_t>(c.x & 0xFFFFu)),
@@ -1058,132 +1168,117 @@ __device__ __forceinline__ float4 codes4_to_f32(uint2 c) {
                        static_cast<float>(static_cast<int16_t>(c.y >> 16)));
 }
 
+// key = sign(c) m of a live range (-inf otherwise): c (m - m*) = |c| (key - max key)
+__device__ __forceinline__ double range_key(const RangeStat& st, bool cpos) {
+    return st.l > 0.0f ? (cpos ? st.m : -st.m) : -INFINITY;
+}
+__device__ __forceinline__ float range_weight(const RangeStat& st, bool cpos, double cabs, double kmax) {
+    return st.l > 0.0f ? __builtin_amdgcn_exp2f(static_cast<float>(cabs * (range_key(st, cpos) - kmax)))
+                       : 0.0f;
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Block = 256 threads = one (b, row) and one quarter (128 columns) of the
+// output row: the largest key and L over all ranges first, then 8 groups of
+// 32 lanes, group g summing the ranges s = g mod 8 (lane = 4 columns), and one
+// reduction over the groups in LDS.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = 8;
 constexpr int kMergeCols = kKvLora / 4;
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const int16_t* __restrict__ part_o,
-                                                                  const float* __restrict__ part_ml,
+                                                                  const RangeStat* __restrict__ part_ml,
                                                                   int B, int QH, int n_splits, float c,
                                                                   float* __restrict__ out) {
-    __shared__ float s_red[kMergeThreads / 64];
+    __shared__ double s_k[kMergeThreads / 64];
+    __shared__ float s_l[kMergeThreads / 64];
     __shared__ float4 s_acc[kMergeGroups][32];
-    __shared__ float s_l[kMergeGroups];
     const int tid = threadIdx.x;
     const int64_t br = blockIdx.x >> 2;  // b * QH + row
     const int col0 = (blockIdx.x & 3) * kMergeCols;
     const int64_t stride = static_cast<int64_t>(B) * QH;
     const bool cpos = c >= 0.0f;
+    const double cabs = fabs(static_cast<double>(c));
 
-    // m*: the largest (c > 0) or smallest (c < 0) reference with l > 0
-    float mm = cpos ? -INFINITY : INFINITY;
-    for (int s = tid; s < n_splits; s += kMergeThreads) {
-        const float2 ml = *reinterpret_cast<const float2*>(part_ml + (s * stride + br) * 4);
-        if (ml.y > 0.0f) mm = cpos ? fmaxf(mm, ml.x) : fminf(mm, ml.x);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(mm, off, 64);
-        mm = cpos ? fmaxf(mm, o) : fminf(mm, o);
-    }
-    if ((tid & 63) == 0) s_red[tid >> 6] = mm;
+    double kmax = -INFINITY;
+    for (int s = tid; s < n_splits; s += kMergeThreads) kmax = fmax(kmax, range_key(part_ml[s * stride + br], cpos));
+    kmax = wave_max_f64(kmax);
+    if ((tid & 63) == 0) s_k[tid >> 6] = kmax;
     __syncthreads();
-    mm = s_red[0];
-#pragma unroll
-    for (int k = 1; k < kMergeThreads / 64; ++k) mm = cpos ? fmaxf(mm, s_red[k]) : fminf(mm, s_red[k]);
-    const bool any = cpos ? mm > -INFINITY : mm < INFINITY;
+    kmax = fmax(fmax(s_k[0], s_k[1]), fmax(s_k[2], s_k[3]));
+    float lsum = 0.0f;
+    if (kmax > -INFINITY) {
+        for (int s = tid; s < n_splits; s += kMergeThreads) {
+            const RangeStat st = part_ml[s * stride + br];
+            lsum += range_weight(st, cpos, cabs, kmax) * st.l;
+        }
+    }
+    lsum = wave_sum_f32(lsum);
+    if ((tid & 63) == 0) s_l[tid >> 6] = lsum;
+    __syncthreads();
+    lsum = (s_l[0] + s_l[1]) + (s_l[2] + s_l[3]);
+    const float inv_l = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 
     const int grp = tid >> 5, q = tid & 31;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lsum = 0.0f;
-    if (any) {
+    if (lsum > 0.0f) {
         const int16_t* po = part_o + br * kKvLora + col0 + 4 * q;
-        int s = grp;
-        // four splits in flight per lane
-        for (; s + 3 * kMergeGroups < n_splits; s += 4 * kMergeGroups) {
-            float4 ml[4];
-            uint2 o[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t su = s + u * kMergeGroups;
-                ml[u] = *reinterpret_cast<const float4*>(part_ml + (su * stride + br) * 4);
-                o[u] = *reinterpret_cast<const uint2*>(po + su * stride * kKvLora);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (ml[u].y > 0.0f) {
-                    const float wgt = __builtin_amdgcn_exp2f(c * (ml[u].x - mm));
-                    lsum += wgt * ml[u].y;
-                    const float4 v = codes4_to_f32(o[u]);
-                    const float ws = wgt * ml[u].z;
-                    acc.x += ws * v.x;
-                    acc.y += ws * v.y;
-                    acc.z += ws * v.z;
-                    acc.w += ws * v.w;
-                }
-            }
-        }
-        for (; s < n_splits; s += kMergeGroups) {
-            const float4 ml = *reinterpret_cast<const float4*>(part_ml + (static_cast<int64_t>(s) * stride + br) * 4);
-            if (ml.y > 0.0f) {
-                const float4 v = codes4_to_f32(
-                    *reinterpret_cast<const uint2*>(po + static_cast<int64_t>(s) * stride * kKvLora));
-                const float wgt = __builtin_amdgcn_exp2f(c * (ml.x - mm));
-                lsum += wgt * ml.y;
-                const float ws = wgt * ml.z;
-                acc.x += ws * v.x;
-                acc.y += ws * v.y;
-                acc.z += ws * v.z;
-                acc.w += ws * v.w;
-            }
+        for (int s = grp; s < n_splits; s += kMergeGroups) {
+            const RangeStat st = part_ml[s * stride + br];
+            const uint2 o = *reinterpret_cast<const uint2*>(po + static_cast<int64_t>(s) * stride * kKvLora);
+            const float ws = range_weight(st, cpos, cabs, kmax) * st.l * inv_l * st.o_scale;
+            const float4 v = codes4_to_f32(o);
+            acc.x += ws * v.x;
+            acc.y += ws * v.y;
+            acc.z += ws * v.z;
+            acc.w += ws * v.w;
         }
     }
     s_acc[grp][q] = acc;
-    if (q == 0) s_l[grp] = lsum;
     __syncthreads();
     if (grp == 0) {
-        float l = 0.0f;
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int g2 = 0; g2 < kMergeGroups; ++g2) {
-            l += s_l[g2];
             const float4 v = s_acc[g2][q];
             a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
         }
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        *reinterpret_cast<float4*>(out + br * kKvLora + col0 + 4 * q) =
-            make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+        *reinterpret_cast<float4*>(out + br * kKvLora + col0 + 4 * q) = a;
     }
 }
 
-// The same merge for at most 64 splits: one wave per (b, row), lane s < n
-// holding split s's (m, l), every lane summing 8 columns over the splits.
+// The same merge for at most 64 ranges: one wave per (b, row), lane s < n
+// holding range s's statistics, every lane summing 8 columns over the ranges.
 constexpr int kMergeRowsPerBlock = 4;
 __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel(
-    const int16_t* __restrict__ part_o, const float* __restrict__ part_ml, int B, int QH,
+    const int16_t* __restrict__ part_o, const RangeStat* __restrict__ part_ml, int B, int QH,
     int n_splits, float c, float* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int64_t br = static_cast<int64_t>(blockIdx.x) * kMergeRowsPerBlock + (threadIdx.x >> 6);
     const int64_t stride = static_cast<int64_t>(B) * QH;
     if (br >= stride) return;
     const bool cpos = c >= 0.0f;
-    float4 ml = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (lane < n_splits) ml = *reinterpret_cast<const float4*>(part_ml + (lane * stride + br) * 4);
-    float mm = ml.y > 0.0f ? ml.x : (cpos ? -INFINITY : INFINITY);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(mm, off, 64);
-        mm = cpos ? fmaxf(mm, o) : fminf(mm, o);
-    }
-    const float wgt = ml.y > 0.0f ? __builtin_amdgcn_exp2f(c * (ml.x - mm)) : 0.0f;
-    float lsum = wgt * ml.y;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-    const float wsc = wgt * ml.z;  // weight of split `lane`'s codes (0 for an empty split)
+    const double cabs = fabs(static_cast<double>(c));
+    RangeStat st{0.0, 0.0f, 0.0f};
+    if (lane < n_splits) st = part_ml[lane * stride + br];
+    const double kmax = wave_max_f64(range_key(st, cpos));
+    const float wgt = kmax > -INFINITY ? range_weight(st, cpos, cabs, kmax) : 0.0f;
+    const float lsum = wave_sum_f32(wgt * st.l);
+    // weight of range `lane`'s codes (0 for an empty range)
+    const float wsc = lsum > 0.0f ? wgt * st.l * (1.0f / lsum) * st.o_scale : 0.0f;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
     const int16_t* po = part_o + br * kKvLora + 8 * lane;
-    // eight splits' codes loaded at once, without branches: every split's
-    // codes are written (an empty split's are zeros) and finite, so a zero
-    // weight adds exactly 0; indices past the last split repeat it with
+    // eight ranges' codes loaded at once, without branches: the codes of an
+    // empty range are not written, but any int16 value is finite, so its zero
+    // weight adds exactly 0; indices past the last range repeat it with
     // weight 0
     for (int s2 = 0; s2 < n_splits; s2 += 8) {
         uint4 o8[8];
@@ -1203,13 +1298,12 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel
             a1.x += w2 * v1.x; a1.y += w2 * v1.y; a1.z += w2 * v1.z; a1.w += w2 * v1.w;
         }
     }
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
     float* o = out + br * kKvLora + 8 * lane;
-    *reinterpret_cast<float4*>(o) = make_float4(a0.x * inv, a0.y * inv, a0.z * inv, a0.w * inv);
-    *reinterpret_cast<float4*>(o + 4) = make_float4(a1.x * inv, a1.y * inv, a1.z * inv, a1.w * inv);
+    *reinterpret_cast<float4*>(o) = a0;
+    *reinterpret_cast<float4*>(o + 4) = a1;
 }
 
-void launch_merge(const int16_t* part_o, const float* part_ml, int B, int QH, int n_splits, float c,
+void launch_merge(const int16_t* part_o, const RangeStat* part_ml, int B, int QH, int n_splits, float c,
                   float* out, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(B) * QH;
     if (n_splits <= 64) {
@@ -1259,7 +1353,8 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) 
                        0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;
     if (d.n_splits > 1 && merge) {
-        launch_merge(a.part_o, a.part_ml, d.B, a.QH, d.n_splits, a.c, d.out, stream);
+        launch_merge(a.part_o, reinterpret_cast<const RangeStat*>(a.part_ml), d.B, a.QH, d.n_splits, a.c,
+                     d.out, stream);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;
@@ -1269,7 +1364,7 @@ int launch_lse_merge(const void* partials, int B, int QH, int n_splits, float so
                      float* out, hipStream_t stream) {
     const size_t rows = static_cast<size_t>(n_splits) * B * QH;
     const int16_t* po = static_cast<const int16_t*>(partials);
-    const float* ml = reinterpret_cast<const float*>(po + rows * kKvLora);
+    const RangeStat* ml = reinterpret_cast<const RangeStat*>(po + rows * kKvLora);
     launch_merge(po, ml, B, QH, n_splits, softmax_scale * 1.4426950408889634f, out, stream);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -18,7 +18,8 @@ int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_r
                                    const float* norm_weight, float eps, const int64_t* positions,
                                    float theta, uint8_t* codes, float* scales,
                                    const int64_t* dst_rows, hipStream_t stream);
-int launch_encode_bits(uint32_t first, uint64_t count, uint8_t* out, hipStream_t stream);
+// encoder 0: the quantizer's conversion; 1: the integer bit-math encoder
+int launch_encode_bits(uint32_t first, uint64_t count, int encoder, uint8_t* out, hipStream_t stream);
 // non-absorbed projection of cache rows (see kv8_project.hip); N a multiple of 128
 int launch_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
                         const uint16_t* w_kv_b, int N, uint16_t* out, float* rope_out,

@@ -275,18 +275,21 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     }
 }
 
-// out[k] = encode(f32 with bit pattern first + k), 4 codes per thread.
+// out[k] = encode(f32 with bit pattern first + k), 4 codes per thread, with
+// the quantizer's conversion (kBitMath false) or the integer encoder.
+template <bool kBitMath>
 __global__ __launch_bounds__(256) void encode_bits_kernel(uint32_t first, uint64_t count,
                                                           uint8_t* __restrict__ out) {
     const uint64_t n4 = (count + 3) / 4;
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
          i += static_cast<uint64_t>(gridDim.x) * 256) {
         const uint64_t k = 4 * i;
-        const uint32_t w = encode4_e4m3_hw(
-            __uint_as_float(static_cast<uint32_t>(first + k)),
-            __uint_as_float(static_cast<uint32_t>(first + k + 1)),
-            __uint_as_float(static_cast<uint32_t>(first + k + 2)),
-            __uint_as_float(static_cast<uint32_t>(first + k + 3)));
+        const float f0 = __uint_as_float(static_cast<uint32_t>(first + k));
+        const float f1 = __uint_as_float(static_cast<uint32_t>(first + k + 1));
+        const float f2 = __uint_as_float(static_cast<uint32_t>(first + k + 2));
+        const float f3 = __uint_as_float(static_cast<uint32_t>(first + k + 3));
+        const uint32_t w = kBitMath ? pack4(encode_e4m3(f0), encode_e4m3(f1), encode_e4m3(f2), encode_e4m3(f3))
+                                    : encode4_e4m3_hw(f0, f1, f2, f3);
         if (k + 4 <= count) {
             reinterpret_cast<uint32_t*>(out)[i] = w;
         } else {
@@ -346,13 +349,17 @@ int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_r
     return launch_rows<true>(src, stride, n_rows, codes, scales, dst_rows, pa, stream);
 }
 
-int launch_encode_bits(uint32_t first, uint64_t count, uint8_t* out, hipStream_t stream) {
+int launch_encode_bits(uint32_t first, uint64_t count, int encoder, uint8_t* out, hipStream_t stream) {
     const uint64_t n4 = (count + 3) / 4;
     uint64_t blocks = (n4 + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     if (blocks == 0) return 0;
-    hipLaunchKernelGGL(encode_bits_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                       stream, first, count, out);
+    if (encoder == 1)
+        hipLaunchKernelGGL(encode_bits_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                           stream, first, count, out);
+    else
+        hipLaunchKernelGGL(encode_bits_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                           stream, first, count, out);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

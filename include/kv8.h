@@ -32,9 +32,12 @@
  *   - `stream` is a hipStream_t (NULL = the default stream); calls are
  *     asynchronous on it and never synchronize the host;
  *   - bf16 values are passed as their uint16_t bit patterns;
- *   - the library keeps no state between calls; kv8_absorb_decode may take
- *     stream-ordered device memory (hipMallocAsync) for split partials and
- *     returns it on the same stream before returning;
+ *   - the library keeps no state between calls.  One call allocates:
+ *     kv8_absorb_decode takes stream-ordered device memory (hipMallocAsync)
+ *     for its split partials and returns it on the same stream before
+ *     returning (its signature has no workspace).  Every other call runs on
+ *     caller memory only; kv8_absorb_decode_splitT and the two-stage form are
+ *     the allocation-free decode calls;
  *   - argument errors are reported synchronously through the return value
  *     and nothing is launched; data is never an error (NaN, inf, zero and
  *     subnormal values have defined results); nothing aborts or prints.
@@ -136,7 +139,25 @@ int kv8_norm_rope_quantize_rows(const float* src, int64_t src_row_stride, int64_
  * visible row t: s_t = softmax_scale * (scale_Lc[t] * (q_lat . dec(Lc_t)) +
  * scale_Rc[t] * (q_rope . dec(Rc_t))); out = sum_t softmax(s)_t *
  * scale_Lc[t] * dec(Lc_t).  Long sequences are split internally and merged
- * by log-sum-exp. */
+ * by log-sum-exp.
+ *
+ * Accuracy (every finite cache and query, any row magnitude): the score and
+ * context products are exact products of the dequantized rows and the bf16
+ * queries summed in f32; scores are formed relative to the largest row scale
+ * of the token range, so they stay finite for rows up to the f32 maximum.
+ * The probabilities enter the context pass as fp16 relative to the range's
+ * largest Lc scale; a range whose Lc scales differ by more than 2^6 is run
+ * watched, and a query row whose largest probability operand falls below
+ * 2^-6 is run again with its operands shifted by up to 2^100, so precision is
+ * lost only when the rows carrying a query's weight have Lc scales more than
+ * 2^100 below the largest one of their range.  Each row's probability
+ * operand is rounded to fp16 once (relative error <= 2^-11); these errors
+ * average out over rows, except when many rows with the same scale and weight
+ * cancel each other in the weighted average, where the error relative to the
+ * output grows with the cancellation factor sum_t w_t |V_t| / |sum_t w_t V_t|.
+ * Weights below 2^-149 of a query row's largest weight are dropped (f32
+ * underflow).  A split adds one 16-bit rounding of each range's normalised
+ * context (see the two-stage form below). */
 int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope,
                       const uint8_t* codes, const float* scales,
                       const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
@@ -173,17 +194,25 @@ int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope,
  * holding different token ranges of one sequence can be merged the same way.
  *
  * Partials buffer (device, caller-owned, 256-byte aligned), R = Q*H:
- *   O  int16 [num_splits][B][R][kv_lora]  codes of
- *                                         sum_t 2^(c (x_t - m)) scale_Lc[t] dec(Lc_t)
- *   ml f32   [num_splits][B][R][4]        m = reference score,
- *                                         l = sum_t 2^(c (x_t - m)), o_scale, 0
- * (ml follows O directly).  O of a row is code * o_scale, with the codes
- * rounded from 32767 O / max |O| over the row (max |O| = 32767 o_scale; a
- * row with O = 0 has o_scale = 0): 16 bits per value with an absolute error
- * of at most max |O| / 65534 on each.  With x_t = q_lat . xhat_Lc[t] +
- * q_rope . xhat_Rc[t] (before softmax_scale), c = softmax_scale * log2(e);
- * a range with no visible row has m = l = o_scale = 0 and its O codes are
- * not written (the merge gives such a range weight 0). */
+ *   V  int16 [num_splits][B][R][kv_lora]  codes of the range's normalised
+ *                                         context V = O / l, with
+ *                                         O = sum_t 2^(c (x_t - m)) scale_Lc[t] dec(Lc_t)
+ *   st 16-byte records [num_splits][B][R] { double m; float l; float v_scale; }:
+ *                                         m = reference score (f64),
+ *                                         l = sum_t 2^(c (x_t - m)),
+ *                                         v_scale = scale of the codes
+ * (st follows V directly).  V of a row is code * v_scale, with the codes
+ * rounded from 32767 V / max |V| over the row (max |V| = 32767 v_scale; a
+ * row with V = 0 has v_scale = 0): 16 bits per value with an absolute error
+ * of at most max |V| / 65534 on each.  V stays within the range of the rows'
+ * values, so every field is finite for every finite cache.  With
+ * x_t = q_lat . xhat_Lc[t] + q_rope . xhat_Rc[t] (before softmax_scale),
+ * c = softmax_scale * log2(e); a range with no visible row has m = l =
+ * v_scale = 0 and its codes are not written (the merge gives it weight 0).
+ * The merge passes the codes' error on as at most max_s max|V_s| / 65534 per
+ * output value: below 1e-3 of the largest output as long as no range's
+ * normalised context exceeds the largest output by more than 65x (that only
+ * happens when ranges cancel each other in the merged average). */
 
 /* Bytes of a partials buffer for these shapes. */
 size_t kv8_partials_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t num_splits);
@@ -195,7 +224,8 @@ int kv8_decode_plan(int32_t B, int32_t Q, int32_t H, int32_t max_len,
 
 /* Stage 1.  Range s of sequence b is rows [s*k, (s+1)*k) of the sequence with
  * k = split_tokens, or k = ceil(kv_len[b] / num_splits) when split_tokens is
- * 0.  Other arguments as kv8_absorb_decode. */
+ * 0.  A fixed split must cover max_len (split_tokens * num_splits >= max_len,
+ * else KV8_EINVAL).  Other arguments as kv8_absorb_decode. */
 int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
                                const uint8_t* codes, const float* scales,
                                const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
@@ -204,11 +234,13 @@ int kv8_absorb_decode_partials(const uint16_t* q_lat, const uint16_t* q_rope,
                                void* partials, size_t partials_bytes, void* stream);
 
 /* Stage 2 ([colibri#299] PR description, follow-up: split-T kernels):
- * out[b][r] = sum_s w_s O_s / sum_s w_s l_s over ranges with l_s > 0,
+ * out[b][r] = sum_s w_s l_s V_s / sum_s w_s l_s over ranges with l_s > 0,
  * w_s = 2^(c (m_s - m*)), m* the reference with the largest c m_s; zero when
- * no range saw a row. */
-int kv8_lse_merge(const void* partials, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
-                  int32_t num_splits, float softmax_scale, float* out, void* stream);
+ * no range saw a row.  partials_bytes (the buffer's size) must be at least
+ * kv8_partials_bytes(B, Q, H, kv_lora, num_splits), else KV8_EWORKSPACE. */
+int kv8_lse_merge(const void* partials, size_t partials_bytes, int32_t B, int32_t Q, int32_t H,
+                  int32_t kv_lora, int32_t num_splits, float softmax_scale, float* out,
+                  void* stream);
 
 /* The non-absorbed consumer of the cache rows ([colibri#299] commit message,
  * attention_rows item: the non-absorbed prefill dequantizes Lc into a staging
@@ -238,9 +270,13 @@ const char* kv8_status_string(int status);
 /* ---- Verification entry points (same device code as the calls above) ---- */
 
 /* out[k] = e4m3 code of the f32 value whose bit pattern is first + k, for
- * k < count (count <= 2^32 - first), with the encoder kv8_quantize_rows uses.
- * out must be 4-byte aligned. */
-int kv8_encode_bits(uint32_t first, uint64_t count, uint8_t* out, void* stream);
+ * k < count (count <= 2^32 - first).  encoder 0: the encoder kv8_quantize_rows
+ * uses (the gfx950 fp8 conversion after a clamp to +-448 and NaN -> +0);
+ * encoder 1: an integer bit-math encoder of the same rules ([colibri#299]
+ * commit message, kv_fp8.h item: round-to-nearest-even bit-math encoder),
+ * kept as a second, independent device implementation.  out must be 4-byte
+ * aligned; other encoder values return KV8_EINVAL. */
+int kv8_encode_bits(uint32_t first, uint64_t count, int32_t encoder, uint8_t* out, void* stream);
 
 /* Decode n codes with the exact conversions the decode kernels use:
  * out_bf16[k], out_f16[k] = bit patterns of dec(codes[k]) as bf16 and fp16. */

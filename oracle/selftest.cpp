@@ -1,7 +1,8 @@
 // Sanitizer self-test of the CPU oracle (test infrastructure only).  Built by
 // oracle/build.py --selftest with -fsanitize=address,undefined; exercises the
-// codec, the quantizer on special rows and the attention in all its modes so
-// that an out-of-bounds access or undefined operation aborts the run.
+// codec, the quantizer on special rows, the attention in all its modes, the
+// producer step and the non-absorbed projection, so that an out-of-bounds
+// access or undefined operation aborts the run.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -83,6 +84,27 @@ int main() {
     CHECK(orc_attention(nullptr, qr.data(), codes.data(), scales.data(), kv_start, kv_len, B, Q, H,
                         KL, KR, 1.0f, 1, nullptr, 0, o1.data(), 1) == -1);
     CHECK(orc_bytes_per_token_layer(KL, KR) == 584);
+
+    // producer step: strided source rows, then the quantizer on its output
+    const int64_t stride = D + 8;
+    std::vector<float> src(static_cast<size_t>(n) * stride, 0.5f), y(static_cast<size_t>(n) * D);
+    for (size_t i = 0; i < rows.size(); ++i) src[(i / D) * stride + i % D] = rows[i];
+    std::vector<float> wnorm(KL);
+    for (int j = 0; j < KL; ++j) wnorm[j] = 0.5f + static_cast<float>(j % 7) / 8.0f;
+    std::vector<int64_t> pos(n);
+    for (int i = 0; i < n; ++i) pos[i] = 1000 * i + 3;
+    orc_norm_rope_rows(src.data(), stride, n, KL, KR, wnorm.data(), 1e-6f, pos.data(), 10000.0f,
+                       y.data(), 3);
+    CHECK(y[0] != 0.0f && std::isnan(y[static_cast<size_t>(3) * D + 5]));  // NaN propagates
+    orc_quantize_rows(y.data(), D, n, KL, KR, codes.data(), scales.data(), nullptr, 2);
+
+    // non-absorbed projection of the quantized rows by a bf16 weight
+    const int N = 24;
+    std::vector<uint16_t> wb(static_cast<size_t>(N) * KL);
+    for (size_t i = 0; i < wb.size(); ++i) wb[i] = bf16(static_cast<float>((i * 31) % 13) / 13.0f - 0.5f);
+    std::vector<double> po(static_cast<size_t>(n) * N), pr(static_cast<size_t>(n) * KR);
+    orc_project_rows(codes.data(), scales.data(), n, KL, KR, wb.data(), N, po.data(), pr.data(), 3);
+    CHECK(po[static_cast<size_t>(1) * N] == 0.0 && pr[static_cast<size_t>(1) * KR] == 0.0);  // zero row
     std::printf("oracle selftest ok\n");
     return 0;
 }

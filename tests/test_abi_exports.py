@@ -48,8 +48,9 @@ def test_argument_errors_are_synchronous():
     assert L.kv8_quantize_rows(None, 576, -1, 512, 64, None, None, None, None) == -1
     assert L.kv8_quantize_rows(None, 576, 4, 512, 64, None, None, None, None) == -1
     assert L.kv8_quantize_rows(None, 576, 0, 512, 64, None, None, None, None) == 0
-    assert L.kv8_encode_bits(0, 0, None, None) == 0
-    assert L.kv8_encode_bits(5, 1 << 32, 16, None) == -1
+    assert L.kv8_encode_bits(0, 0, 0, None, None) == 0
+    assert L.kv8_encode_bits(5, 1 << 32, 0, 16, None) == -1
+    assert L.kv8_encode_bits(0, 4, 2, 16, None) == -1
     assert L.kv8_decode_codes(None, -3, None, None, None) == -1
 
 
@@ -94,3 +95,30 @@ def test_decode_plan():
         assert k % 32 == 0 or n == 1
         assert n * k >= T and (n - 1) * k < T
         assert n == 1 or k <= 4096
+
+
+def test_two_stage_calls_check_sizes_before_any_gpu_work():
+    """The merge rejects a partials buffer smaller than its shapes need, and a
+    fixed-size split that does not cover max_len is an argument error (it
+    would drop the tail rows)."""
+    if not os.path.exists(kv8.LIB_PATH):
+        pytest.skip("libkv8.so not built")
+    L = kv8.lib()
+    f32 = ctypes.c_float
+    need = L.kv8_partials_bytes(2, 1, 128, 512, 8)
+    assert need == 8 * 2 * 128 * (512 * 2 + 16)
+    fake = ctypes.c_void_p(1 << 20)  # (never dereferenced: the checks come first)
+    merge = L.kv8_lse_merge
+    assert merge(fake, need - 1, 2, 1, 128, 512, 8, f32(0.04), fake, None) == -4
+    assert merge(fake, need, 2, 1, 128, 500, 8, f32(0.04), fake, None) == -2
+    assert merge(fake, need, 2, 1, 128, 512, 0, f32(0.04), fake, None) == -1
+    assert merge(None, need, 2, 1, 128, 512, 8, f32(0.04), fake, None) == -1
+    assert merge(fake, need, 2, 1, 128, 512, 8, f32(float("nan")), fake, None) == -1
+    part = L.kv8_absorb_decode_partials
+    args = [fake] * 6
+    # 3 ranges of 1,024 rows cannot cover max_len 4,000
+    assert part(*args, 4000, 2, 1, 128, 512, 64, f32(0.04), 1024, 3, fake,
+                L.kv8_partials_bytes(2, 1, 128, 512, 3), None) == -1
+    # too small a buffer for the ranges asked for
+    assert part(*args, 4000, 2, 1, 128, 512, 64, f32(0.04), 1024, 4, fake,
+                L.kv8_partials_bytes(2, 1, 128, 512, 3), None) == -4

@@ -126,17 +126,126 @@ def test_empty_and_short_sequences(kv8):
 
 
 def test_extreme_row_scales(kv8):
-    """Sequences whose rows have amax near 1e-30, 1 and 1e30 (scales far outside
-    the fp16 range of the probabilities), and inside one sequence guarded
-    (all-zero) rows next to rows a thousand times larger than the rest."""
-    w = workloads.tiny(seed=6, B=3, Q=1, H=32, T=200, outlier_p=0.0)
-    mult = np.array([1e-30, 1.0, 1e30], np.float32)
-    for b in range(3):
-        w.rows[b * 200:(b + 1) * 200] *= mult[b]
+    """Rows of every finite magnitude: sequences whose rows have amax near
+    1e-30, 1, 1e30, 1e34 and 1e36, one row at amax 3e38, a sequence with
+    queries times 1e30 over rows times 1e30 (scores far beyond the f32
+    range), and guarded (all-zero) rows next to rows a thousand times larger
+    than the rest.  Direct output and split partials; every output finite."""
+    T = 200
+    mult = np.array([1e-30, 1.0, 1e30, 1e34, 1e36, 1.0, 1e30], np.float32)
+    B = len(mult)
+    w = workloads.tiny(seed=6, B=B, Q=1, H=32, T=T, outlier_p=0.0)
+    for b in range(B):
+        w.rows[b * T:(b + 1) * T] *= mult[b]
     w.rows[210:215] = 0.0
     w.rows[220] *= np.float32(1e3)
     w.rows[390] *= np.float32(1e3)
+    r = 5 * T + 77  # one row at amax 3e38 (it dominates its sequence)
+    w.rows[r] *= np.float32(3e38) / np.abs(w.rows[r]).max()
+    ql = workloads.bf16_to_f32(w.q_lat)
+    ql[6] *= np.float32(1e30)
+    w.q_lat = workloads.bf16_bits(ql)
+    assert np.all(np.isfinite(w.rows))
+    cache = build_cache(kv8, w.rows)
+    run_case(kv8, w, cache=cache)
+    run_case(kv8, w, splits=3, cache=cache)
+
+
+def _unit(v):
+    return v / np.linalg.norm(v, axis=-1, keepdims=True)
+
+
+def test_small_lc_scales_carry_the_weight(kv8):
+    """Every row but one is 2^-20 times smaller than the remaining row, whose
+    scores are about -200 for every head: the weight sits on rows whose Lc
+    scale is ~2^-27 of the range's largest, far below the fp16 range of the
+    probability operands unless they are shifted (watched range)."""
+    w = workloads.tiny(seed=30, B=1, Q=1, H=16, T=300, outlier_p=0.0)
+    w.rows *= np.float32(2.0 ** -20)
+    q = workloads.bf16_to_f32(w.q_lat[0, 0])
+    w.rows[150, :KL] = -5000.0 * _unit(q).sum(0)
     run_case(kv8, w)
+    run_case(kv8, w, splits=2)
+
+
+def test_dominant_row_with_small_lc_scale(kv8):
+    """One row scores ~40 above every other row through its Rc part while its
+    Lc scale is 2^-20 of the range's largest: its probability operand would
+    be an fp16 subnormal without the shift."""
+    w = workloads.tiny(seed=31, B=1, Q=1, H=16, T=300, outlier_p=0.0)
+    qr = workloads.bf16_to_f32(w.q_rope)
+    qr[0, 0, :] = qr[0, 0, 0]  # one rope direction for every head
+    w.q_rope = workloads.bf16_bits(qr)
+    d = 120
+    w.rows[d, :KL] *= np.float32(2.0 ** -20)
+    u = qr[0, 0, 0]
+    w.rows[d, KL:] = (40.0 * 24.0 / np.linalg.norm(u)) * _unit(u)
+    got, ref = run_case(kv8, w)
+    # the result is the dominant row's (tiny) Lc, not zero
+    assert np.abs(ref).max() < 1e-5 and np.abs(got).max() > 0.5 * np.abs(ref).max()
+    run_case(kv8, w, splits=3)
+
+
+def test_guarded_rows_as_reference(kv8):
+    """All-zero (guarded, scale 0) rows score 0 while every other row scores
+    about -15: the reference rows carry no Lc, and the rows that make the
+    output have probability operands near 2^-22."""
+    w = workloads.tiny(seed=32, B=1, Q=1, H=16, T=300, outlier_p=0.0)
+    ql = workloads.bf16_to_f32(w.q_lat)
+    ql[0, 0, :] = ql[0, 0, 0]
+    w.q_lat = workloads.bf16_bits(ql)
+    w.q_rope[:] = 0
+    q = ql[0, 0, 0]
+    rng = np.random.default_rng(33)
+    w.rows[:, :KL] = -(15.0 * 24.0 / np.linalg.norm(q)) * _unit(q) + \
+        0.1 * rng.standard_normal((w.rows.shape[0], KL)).astype(np.float32)
+    w.rows[50:55] = 0.0
+    run_case(kv8, w)
+    run_case(kv8, w, splits=4)
+
+
+def test_cancelling_ranges_within_the_partials_bound(kv8):
+    """Cancellation across ranges, for the 16-bit partials: the rows are c_t U
+    with c_t ~ U[0.9, 1.1] in the first half and U[-1.0, -0.8] in the second,
+    under a uniform softmax (zero queries).  Every range's normalised context
+    then points along dec(U), so its 16-bit codes (and their rounding) are the
+    same in every range, while the merged output ~0.05 U is 20x smaller than
+    each range's context: inside the partials' bound (65x for the 1e-3 bar).
+    (The per-token fp16 rounding of the probability operands differs from row
+    to row here, because the row scales differ, and averages out.)"""
+    w = workloads.tiny(seed=34, B=1, Q=1, H=16, T=2048, outlier_p=0.0)
+    w.q_lat[:] = 0
+    w.q_rope[:] = 0
+    rng = np.random.default_rng(35)
+    u = rng.standard_normal(D).astype(np.float32)
+    c = np.concatenate([rng.uniform(0.9, 1.1, 1024), rng.uniform(-1.0, -0.8, 1024)]).astype(np.float32)
+    w.rows[:] = c[:, None] * u[None, :]
+    got, ref = run_case(kv8, w, splits=2)
+    ratio = np.abs(u[:KL]).max() / np.abs(ref).max()
+    say("  range context / merged output: %.1f" % ratio)
+    assert 10.0 < ratio < 65.0
+
+
+@pytest.mark.parametrize("T", [96, 3072])
+def test_tile_count_multiple_of_three(kv8, T):
+    """3 and 96 tiles of 32 rows (the last iteration then re-copies into the
+    buffer the epilogue reuses): the direct output (B=128, H=256: 256 blocks,
+    one range each) and the partials of one range merged."""
+    w = workloads.tiny(seed=36, B=128, Q=1, H=256, T=T, outlier_p=0.0)
+    cache = build_cache(kv8, w.rows, check=False)
+    sel = sample_rows(w.B, w.Q, w.H, 256, 37)
+    run_case(kv8, w, splits=1, sel=sel, cache=cache)
+    codes, scales, c, s = cache
+    ql, qr, st, ln = to_dev(w)
+    part = torch.empty(kv8.partials_bytes(w.B, w.Q, w.H, 1) // 4, dtype=torch.float32, device="cuda")
+    kv8.absorb_decode_partials(ql, qr, codes, scales, st, ln, w.max_len, w.softmax_scale, 0, 1, part)
+    out = kv8.lse_merge(part, w.B, w.Q, w.H, 1, w.softmax_scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention(w.q_lat, w.q_rope, c, s, w.kv_start, w.kv_len, Q=w.Q,
+                           softmax_scale=w.softmax_scale, sel=sel)
+    e = rel_err(out.cpu().numpy().reshape(-1, KL)[sel], ref.reshape(-1, KL))
+    say("  partials: max|d|/max|ref| = %.3g" % e)
+    assert e <= TOL, e
 
 
 def test_reference_raise_restart(kv8):
@@ -192,23 +301,35 @@ def sample_rows(B, Q, H, n, seed):
     return np.sort(rng.choice(B * Q * H, size=min(n, B * Q * H), replace=False)).astype(np.int64)
 
 
-def test_batched_full_size_sampled(kv8):
-    """B=32, T=8192, H=128 (the bench launch), 96 sampled output rows."""
+def test_batched_full_size_every_row(kv8):
+    """B=32, T=8192, H=128 (the benchmark launch), all 4,096 output rows."""
     w = workloads.batched(seed=0)
-    run_case(kv8, w, sel=sample_rows(w.B, w.Q, w.H, 96, 11))
+    run_case(kv8, w)
 
 
-def test_long_context_splitT_full_size_sampled(kv8):
+def test_long_context_splitT_full_size_every_row(kv8):
     """B=1, T=262144, H=128, 64 split ranges merged by log-sum-exp; planted
-    strong matches make the softmax peaked."""
+    strong matches make the softmax peaked.  All 128 output rows."""
     w = workloads.long_context(seed=0)
-    run_case(kv8, w, splits=64, sel=sample_rows(1, 1, w.H, 24, 12))
+    run_case(kv8, w, splits=64)
 
 
-def test_ragged_full_size_sampled(kv8):
-    """B=64, lengths U[1k, 64k], Q=4 causal, whole cache quantized on the GPU."""
+def ragged_subset(w, n=8):
+    """Every output row (all Q positions and heads) of n sequences spread over
+    the length range: the sequences at ranks 0, 8, ... of the sorted lengths."""
+    order = np.argsort(w.kv_len, kind="stable")[:: max(1, w.B // n)][:n]
+    seqs = np.sort(order)
+    rows = [(b * w.Q + i) * w.H + h for b in seqs for i in range(w.Q) for h in range(w.H)]
+    return seqs, np.array(rows, np.int64)
+
+
+def test_ragged_full_size_subset_every_row(kv8):
+    """B=64, lengths U[1k, 64k], Q=4 causal, whole cache quantized on the GPU;
+    every row of 8 sequences spread over the length range (4,096 rows)."""
     w = workloads.ragged(seed=0)
-    run_case(kv8, w, sel=sample_rows(w.B, w.Q, w.H, 48, 13))
+    seqs, sel = ragged_subset(w)
+    say("  ragged subset: sequences %s, lengths %s" % (list(seqs), list(w.kv_len[seqs])))
+    run_case(kv8, w, sel=sel)
 
 
 def test_two_stage_equals_single_call(kv8):

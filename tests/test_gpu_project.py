@@ -91,20 +91,23 @@ def test_project_slice_of_cache_and_no_rope(kv8):
     check(c[200:530], s[200:530], wbits, np.arange(330), out, None)
 
 
-def test_project_full_size_sampled(kv8):
-    """8,192 rows (one 8k-token sequence) x N = 32,768 (128 heads x (128 + 128)),
-    compared on 48 sampled rows over every column."""
+def test_project_full_size(kv8):
+    """8,192 rows (one 8k-token sequence) x N = 32,768 (128 heads x (128 + 128)):
+    every row of the first 128-column tile set, and 48 sampled rows over every
+    column."""
     n, N = 8192, 32768
     say("project: full size n=%d N=%d" % (n, N))
     codes, scales, c, s = gpu_cache(kv8, n, 52)
     wb, wbits = weights(N, 53)
     out, rope = kv8.project_rows(codes, scales, wb)
     torch.cuda.synchronize()
+    e0 = check(c, s, wbits[:128], np.arange(n), out[:, :128], rope)
+    say("  columns 0..127, every row: max |err| / max |ref| = %.2e" % e0)
     rows = np.sort(np.random.default_rng(54).choice(n, 48, replace=False))
     ot = out[torch.from_numpy(rows).cuda()]
     rt = rope[torch.from_numpy(rows).cuda()]
     e = check(c, s, wbits, rows, ot, rt)
-    say("  max |err| / max |ref| = %.2e" % e)
+    say("  48 rows, every column: max |err| / max |ref| = %.2e" % e)
 
 
 def test_project_argument_errors(kv8):

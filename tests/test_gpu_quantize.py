@@ -49,19 +49,22 @@ def test_decode_all_codes_exact(kv8):
 
 
 def test_encoder_exhaustive_all_f32(kv8):
-    """Every one of the 2^32 f32 bit patterns, device encoder vs oracle."""
+    """Every one of the 2^32 f32 bit patterns, vs the oracle: the encoder the
+    quantizer uses (the gfx950 conversion behind the clamp, encoder 0) and the
+    integer bit-math encoder (encoder 1)."""
     chunk = 1 << 28
     dev = torch.empty(chunk, dtype=torch.uint8, device="cuda")
     ref = np.empty(chunk, dtype=np.uint8)
     for first in range(0, 1 << 32, chunk):
-        say("encode_bits: first=0x%08x count=%d" % (first, chunk))
-        kv8.encode_bits(first, chunk, dev)
         oracle.encode_bits_range(first, chunk, out=ref)
-        got = dev.cpu().numpy()
-        if not np.array_equal(got, ref):
-            bad = np.flatnonzero(got != ref)[:10]
-            raise AssertionError("mismatch at bit patterns %s: gpu %s oracle %s" % (
-                [hex(first + int(b)) for b in bad], got[bad].tolist(), ref[bad].tolist()))
+        for enc in (0, 1):
+            say("encode_bits: encoder %d first=0x%08x count=%d" % (enc, first, chunk))
+            kv8.encode_bits(first, chunk, dev, encoder=enc)
+            got = dev.cpu().numpy()
+            if not np.array_equal(got, ref):
+                bad = np.flatnonzero(got != ref)[:10]
+                raise AssertionError("encoder %d: mismatch at bit patterns %s: gpu %s oracle %s" % (
+                    enc, [hex(first + int(b)) for b in bad], got[bad].tolist(), ref[bad].tolist()))
 
 
 def quantize_on_gpu(kv8, rows, n_cache=None, dst=None):

@@ -196,3 +196,37 @@ def test_bulk_special_rows_small():
         assert np.all((scales[rr] == 0) == (amax < 1.3166e-36))
     rr = idx["guard_subnormal_entries"]
     assert np.all(scales[rr] > 0)
+
+
+def _torch_codes(x, via_inverse):
+    """Codes of a plain per-segment reading built from numpy f32 arithmetic and
+    torch's float8_e4m3fn cast (a library RNE conversion; every value here is
+    finite and within 448 (1 + 2^-23), which the cast takes to at most 448)."""
+    torch = pytest.importorskip("torch")
+    out = np.empty(x.shape, np.uint8)
+    for a, b in ((0, 512), (512, 576)):
+        seg = x[:, a:b]
+        amax = np.abs(seg).max(1, keepdims=True).astype(np.float32)
+        if via_inverse:
+            q = (seg * (np.float32(448.0) / amax).astype(np.float32)).astype(np.float32)
+        else:
+            q = (seg / (amax / np.float32(448.0)).astype(np.float32)).astype(np.float32)
+        out[:, a:b] = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out
+
+
+def test_codes_come_from_the_inverse_not_the_division():
+    """Reading Q7 (the page's overflow guard forms 448/amax): each code is
+    E(fl32(x * fl32(448/amax))).  On 20,000 Gaussian rows the oracle equals
+    that reading through torch's e4m3 cast everywhere, and the other reading,
+    E(fl32(x / fl32(amax/448))), differs from it on some codes (so this test
+    tells the two apart)."""
+    x = np.random.default_rng(77).standard_normal((20000, 576)).astype(np.float32)
+    codes, _ = oracle.quantize_rows(x)
+    inv_reading = _torch_codes(x, True)
+    div_reading = _torch_codes(x, False)
+    assert np.array_equal(codes, inv_reading)
+    differ = np.argwhere(inv_reading != div_reading)
+    assert len(differ) > 0
+    for r, c in differ:
+        assert codes[r, c] == inv_reading[r, c] != div_reading[r, c]

@@ -27,7 +27,8 @@ _STATUS = {0: "KV8_OK", -1: "KV8_EINVAL", -2: "KV8_EUNSUPPORTED", -3: "KV8_ELAUN
 EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_project_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
            "kv8_absorb_decode_splitT", "kv8_partials_bytes", "kv8_decode_plan",
            "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
-           "kv8_encode_bits", "kv8_decode_codes")
+           "kv8_encode_bits", "kv8_decode_codes", "kv8_absorb_decode_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KV8_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -62,6 +63,8 @@ def lib():
     dec = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
     L.kv8_absorb_decode.restype = ctypes.c_int
     L.kv8_absorb_decode.argtypes = dec + [vp]
+    L.kv8_absorb_decode_noalloc.restype = ctypes.c_int
+    L.kv8_absorb_decode_noalloc.argtypes = dec + [vp]
     L.kv8_splitT_workspace_bytes.restype = sz
     L.kv8_splitT_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.kv8_absorb_decode_splitT.restype = ctypes.c_int
@@ -234,6 +237,17 @@ def absorb_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, softm
     """Absorbed-MLA decode over the fp8 cache; returns out f32 [B,Q,H,512]."""
     args, out, po = _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out)
     _call("kv8_absorb_decode", *args, ctypes.c_float(softmax_scale), po, _stream(stream))
+    return out
+
+
+def absorb_decode_noalloc(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len,
+                          softmax_scale, out=None, stream=None):
+    """absorb_decode without any device allocation in the call: the split
+    partials live in the library's static 64 MiB device array (shared by every
+    call on the device; overlapping calls race).  Pass `out` to avoid the
+    output allocation too."""
+    args, out, po = _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out)
+    _call("kv8_absorb_decode_noalloc", *args, ctypes.c_float(softmax_scale), po, _stream(stream))
     return out
 
 

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kv8_internal.hpp"
 
 namespace {
@@ -290,3 +292,54 @@ int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope, cons
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the split partials live in a static device array.
+// ---------------------------------------------------------------------------
+namespace {
+
+// The array's name is a host-side stand-in in host code; kernels get its
+// device address, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[KV8_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (first call on a device:
+// hipGetSymbolAddress with that device current), or nullptr on failure.
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+}  // namespace
+
+extern "C" int kv8_absorb_decode_noalloc(const uint16_t* q_lat, const uint16_t* q_rope,
+                                         const uint8_t* codes, const float* scales,
+                                         const int64_t* kv_start, const int32_t* kv_len,
+                                         int32_t max_len, int32_t B, int32_t Q, int32_t H,
+                                         int32_t kv_lora, int32_t rope, float softmax_scale,
+                                         float* out, void* stream) {
+    int rc = check_decode(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, B, Q, H,
+                          kv_lora, rope, softmax_scale, out);
+    if (rc != KV8_OK) return rc;
+    kv8::DecodeLaunch d =
+        make_launch(q_lat, q_rope, codes, scales, kv_start, kv_len, B, Q, H, softmax_scale, out);
+    int32_t chunk = 0, splits = 1;
+    kv8_decode_plan(B, Q, H, max_len, &chunk, &splits);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (splits <= 1) return launched(kv8::launch_absorb_decode(d, st));
+    // the same split as kv8_absorb_decode, so the results are the same
+    if (kv8::splitT_workspace_bytes(B, Q, H, splits) > KV8_NOALLOC_SCRATCH_BYTES) return KV8_EWORKSPACE;
+    void* ws = scratch_on_current_device();
+    if (ws == nullptr) return KV8_ELAUNCH;
+    d.n_splits = splits;
+    d.split_chunk = chunk;
+    d.workspace = ws;
+    return launched(kv8::launch_absorb_decode(d, st));
+}

@@ -164,6 +164,32 @@ int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope,
                       int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
                       float softmax_scale, float* out, void* stream);
 
+/* Size of the static device array kv8_absorb_decode_noalloc keeps its split
+ * partials in (64 MiB per device the library runs on, held until the process
+ * ends). */
+#define KV8_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kv8_absorb_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, split plan, kernels and results, but the
+ * split partials live in a static device array of KV8_NOALLOC_SCRATCH_BYTES
+ * instead of stream-ordered memory; the call allocates nothing.  The array's
+ * device address is looked up on the first call on each device (with that
+ * device current; `stream` must belong to the current device).
+ * Returns KV8_EWORKSPACE when the plan's partials,
+ * kv8_partials_bytes(B, Q, H, kv_lora, n) with n from kv8_decode_plan, exceed
+ * KV8_NOALLOC_SCRATCH_BYTES (e.g. B*Q*H*n above 64,527 rows x ranges), and
+ * KV8_ELAUNCH when the address lookup fails.  Every call on one device shares
+ * its array: calls that overlap on one device (different streams, or host
+ * threads) race and must be serialised by the caller.  No part of the array
+ * needs clearing between calls (every value a call reads was written by the
+ * same call, or is given weight 0). */
+int kv8_absorb_decode_noalloc(const uint16_t* q_lat, const uint16_t* q_rope,
+                              const uint8_t* codes, const float* scales,
+                              const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
+                              int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                              float softmax_scale, float* out, void* stream);
+
 /* Bytes of workspace kv8_absorb_decode_splitT needs for these shapes. */
 size_t kv8_splitT_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
                                   int32_t num_splits);

@@ -21,13 +21,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkv8.so")
 
 _STATUS = {0: "KV8_OK", -1: "KV8_EINVAL", -2: "KV8_EUNSUPPORTED", -3: "KV8_ELAUNCH",
-           -4: "KV8_EWORKSPACE", -5: "KV8_ENOMEM"}
+           -4: "KV8_EWORKSPACE", -5: "KV8_ENOMEM", -6: "KV8_EIO", -7: "KV8_EFORMAT"}
 
 # every symbol include/kv8.h declares
 EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_project_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
            "kv8_absorb_decode_splitT", "kv8_partials_bytes", "kv8_decode_plan",
            "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
-           "kv8_encode_bits", "kv8_decode_codes", "kv8_absorb_decode_noalloc")
+           "kv8_encode_bits", "kv8_decode_codes", "kv8_absorb_decode_noalloc",
+           # include/kv8_pool.h (bound in store.py)
+           "kv8_pool_bytes", "kv8_pool_slot_tokens_for", "kv8_store_open", "kv8_store_info",
+           "kv8_store_read", "kv8_store_append", "kv8_store_close", "kv8_store_write_f32",
+           "kv8_pool_create", "kv8_pool_destroy", "kv8_pool_used_bytes", "kv8_pool_layer",
+           "kv8_pool_slot_row", "kv8_pool_len", "kv8_pool_set_len", "kv8_pool_load", "kv8_pool_save")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KV8_NOALLOC_SCRATCH_BYTES
 
 _lib = None

@@ -26,7 +26,9 @@ const char* kv8_status_string(int status) {
         case KV8_EUNSUPPORTED: return "unsupported shape (kv_lora must be 512, rope 64)";
         case KV8_ELAUNCH: return "HIP launch failed";
         case KV8_EWORKSPACE: return "split-T workspace missing or too small";
-        case KV8_ENOMEM: return "device allocation of split partials failed";
+        case KV8_ENOMEM: return "device allocation failed";
+        case KV8_EIO: return "file system call failed";
+        case KV8_EFORMAT: return "not a kv8 store, torn header, or other dimensions";
         default: return "unknown kv8 status";
     }
 }

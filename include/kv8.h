@@ -61,7 +61,9 @@ typedef enum {
     KV8_EUNSUPPORTED = -2,  /* valid but unsupported shape (kv_lora != 512, rope != 64) */
     KV8_ELAUNCH = -3,       /* a HIP launch or runtime call failed */
     KV8_EWORKSPACE = -4,    /* split-T workspace missing or too small */
-    KV8_ENOMEM = -5         /* stream-ordered allocation of split partials failed */
+    KV8_ENOMEM = -5,        /* a device allocation failed */
+    KV8_EIO = -6,           /* a file system call failed (kv8_pool.h stores) */
+    KV8_EFORMAT = -7        /* not a kv8 store, torn header, or other dimensions */
 } kv8_status;
 
 /* Quantize f32 latent token rows into the fp8 cache ([colibri#299] commit

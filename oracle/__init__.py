@@ -60,6 +60,13 @@ def lib():
     L.orc_project_rows.restype = None
     L.orc_project_rows.argtypes = [_u8p, _f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                    _u16p, ctypes.c_int32, _f64p, _f64p, ctypes.c_int]
+    L.orc_quantize_rows_mx.restype = None
+    L.orc_quantize_rows_mx.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int32, _u8p, _u8p, _i64p, ctypes.c_int]
+    L.orc_attention_mx.restype = ctypes.c_int
+    L.orc_attention_mx.argtypes = att + [_u8p, _u8p] + tail
+    L.orc_bytes_per_token_layer_mx.restype = ctypes.c_int64
+    L.orc_bytes_per_token_layer_mx.argtypes = [ctypes.c_int32, ctypes.c_int32]
     L.orc_bytes_per_token_layer.restype = ctypes.c_int64
     L.orc_bytes_per_token_layer.argtypes = [ctypes.c_int32, ctypes.c_int32]
     _lib = L
@@ -223,3 +230,55 @@ def attention_f32rows(q_lat, q_rope, rows, kv_start, kv_len, Q=1,
 
 def bytes_per_token_layer(kv_lora=512, rope=64):
     return int(lib().orc_bytes_per_token_layer(kv_lora, rope))
+
+
+def quantize_rows_mx(src, kv_lora=512, rope=64, dst_rows=None, n_cache_rows=None,
+                     codes=None, exps=None, threads=0):
+    """Block-scaled quantizer: f32 rows [n, >= kv_lora+rope] -> (codes uint8
+    [rows, D], exps uint8 [rows, D/32]: ue8m0 bytes, scale 2^(byte-127))."""
+    a = np.asarray(src, dtype=np.float32)
+    assert a.ndim == 2 and a.strides[1] == 4
+    n = a.shape[0]
+    D = kv_lora + rope
+    rows = n if n_cache_rows is None else n_cache_rows
+    if codes is None:
+        codes = np.zeros((rows, D), dtype=np.uint8)
+    if exps is None:
+        exps = np.zeros((rows, D // 32), dtype=np.uint8)
+    dp = None
+    if dst_rows is not None:
+        dst_rows = np.ascontiguousarray(dst_rows, dtype=np.int64)
+        dp = _p(dst_rows, _i64p)
+    lib().orc_quantize_rows_mx(_p(a, _f32p), a.strides[0] // 4, n, kv_lora, rope,
+                               _p(codes, _u8p), _p(exps, _u8p), dp, _t(threads))
+    return codes, exps
+
+
+def dequantize_mx(codes, exps):
+    """f64 values of block-scaled rows: decode(code) * 2^(exp byte - 127)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    e = np.repeat(np.ascontiguousarray(exps, dtype=np.int64) - 127, 32, axis=-1)
+    table = decode(np.arange(256, dtype=np.uint8))
+    return np.ldexp(table[c], e)
+
+
+def attention_mx(q_lat, q_rope, codes, exps, kv_start, kv_len, Q=1,
+                 softmax_scale=np.float32(1.0 / 24.0), num_splits=1, sel=None, threads=0):
+    """Absorbed decode over dequantized block-scaled rows, f64."""
+    q_lat, q_rope, kv_start, kv_len, B, H, kv_lora, rope, sel, out = _attn_common(
+        q_lat, q_rope, kv_start, kv_len, Q, sel)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    exps = np.ascontiguousarray(exps, dtype=np.uint8)
+    assert codes.shape[-1] == kv_lora + rope and exps.shape[-1] == (kv_lora + rope) // 32
+    rc = lib().orc_attention_mx(_p(q_lat, _u16p), _p(q_rope, _u16p), _p(codes, _u8p),
+                                _p(exps, _u8p), _p(kv_start, _i64p), _p(kv_len, _i32p),
+                                B, Q, H, kv_lora, rope, float(softmax_scale), num_splits,
+                                None if sel is None else _p(sel, _i64p),
+                                0 if sel is None else sel.size, _p(out, _f64p), _t(threads))
+    if rc != 0:
+        raise ValueError("orc_attention_mx: bad arguments")
+    return out
+
+
+def bytes_per_token_layer_mx(kv_lora=512, rope=64):
+    return int(lib().orc_bytes_per_token_layer_mx(kv_lora, rope))

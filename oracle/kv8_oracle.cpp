@@ -394,6 +394,69 @@ void orc_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
     });
 }
 
+// Block-scaled variant (page "Phase 0 toward V4.1 on a 128 GB Mac: lossless
+// mxfp8 residents and kill-test tooling", mxfp8 residents paragraph: e4m3
+// bytes with a ue8m0 exponent per 32-wide group).  The exponent is found by
+// counting: the smallest integer E with amax <= 448 * 2^E (compared exactly
+// in f64), within the ue8m0 range.
+static int mx_block_exponent(const float* x, int32_t w) {
+    double amax = 0.0;
+    for (int32_t i = 0; i < w; ++i)
+        if (std::isfinite(x[i])) amax = std::max(amax, std::fabs(static_cast<double>(x[i])));
+    int E = -127;
+    while (E < 127 && amax > 448.0 * std::ldexp(1.0, E)) ++E;
+    return E;
+}
+
+void orc_quantize_rows_mx(const float* src, int64_t src_row_stride, int64_t n_rows,
+                          int32_t kv_lora, int32_t rope, uint8_t* codes, uint8_t* exps,
+                          const int64_t* dst_rows, int threads) {
+    const int32_t D = kv_lora + rope;
+    const int32_t nb = D / 32;
+    parallel_for(n_rows, threads, [&](int64_t i) {
+        const float* x = src + i * src_row_stride;
+        const int64_t d = dst_rows ? dst_rows[i] : i;
+        for (int32_t b = 0; b < nb; ++b) {
+            const float* xb = x + 32 * b;
+            const int E = mx_block_exponent(xb, 32);
+            exps[d * nb + b] = static_cast<uint8_t>(E + 127);
+            for (int32_t j = 0; j < 32; ++j) {
+                // x * 2^-E in f64 is exact; its f32 rounding only matters below
+                // the smallest e4m3 step, where every value encodes to +-0
+                const float q = static_cast<float>(std::ldexp(static_cast<double>(xb[j]), -E));
+                codes[d * D + 32 * b + j] = orc_encode(q);
+            }
+        }
+    });
+}
+
+int orc_attention_mx(const uint16_t* q_lat, const uint16_t* q_rope,
+                     const uint8_t* codes, const uint8_t* exps,
+                     const int64_t* kv_start, const int32_t* kv_len,
+                     int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                     float softmax_scale, int32_t num_splits,
+                     const int64_t* sel, int64_t n_sel, double* out, int threads) {
+    if (bad_args(q_lat, q_rope, codes, kv_start, kv_len, B, Q, H, kv_lora, rope, out) || !exps ||
+        (sel && n_sel < 0) || (kv_lora + rope) % 32 != 0)
+        return -1;
+    const int64_t D = static_cast<int64_t>(kv_lora) + rope;
+    const int64_t nb = D / 32;
+    const double* dec = tables().all;
+    run_attention(q_lat, q_rope, kv_len, B, Q, H, kv_lora, rope, softmax_scale, num_splits,
+                  sel, n_sel, out, threads, [&](int64_t b) {
+                      const int64_t base = kv_start[b];
+                      return [=](int64_t t, int32_t j) {
+                          const int64_t r = base + t;
+                          return std::ldexp(dec[codes[r * D + j]], static_cast<int>(exps[r * nb + j / 32]) - 127);
+                      };
+                  });
+    return 0;
+}
+
+int64_t orc_bytes_per_token_layer_mx(int32_t kv_lora, int32_t rope) {
+    return static_cast<int64_t>(kv_lora) + rope + (static_cast<int64_t>(kv_lora) + rope) / 32;
+}
+
 int64_t orc_bytes_per_token_layer(int32_t kv_lora, int32_t rope) {
     return static_cast<int64_t>(kv_lora) + rope + 2 * static_cast<int64_t>(sizeof(float));
 }

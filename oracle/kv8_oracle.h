@@ -104,9 +104,34 @@ void orc_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
                       int32_t kv_lora, int32_t rope, const uint16_t* w_bf16, int32_t N,
                       double* out, double* rope_out, int threads);
 
+/* Block-scaled (MX) variant of the row quantizer: the row is cut into blocks of
+ * 32 values (kv_lora and rope multiples of 32), each with one power-of-two
+ * scale 2^E stored as the ue8m0 byte E + 127 (the e4m3 bytes + ue8m0 exponents
+ * of the mxfp8 format named on the page "Phase 0 toward V4.1 on a 128 GB Mac:
+ * lossless mxfp8 residents and kill-test tooling" (keep PR #3), mxfp8
+ * residents paragraph).  Per block: amax over finite entries; E is the
+ * smallest integer with amax <= 448 * 2^E, clamped to [-127, 127] (so a
+ * finite value never saturates, as in the per-row quantizer); codes are
+ * E(x * 2^-E) with the saturating encoder.  Row i goes to cache row
+ * dst_rows[i] (or i): codes[dst][0..kv_lora+rope), exps[dst][0..(kv_lora+rope)/32). */
+void orc_quantize_rows_mx(const float* src, int64_t src_row_stride, int64_t n_rows,
+                          int32_t kv_lora, int32_t rope, uint8_t* codes, uint8_t* exps,
+                          const int64_t* dst_rows, int threads);
+
+/* orc_attention over block-scaled rows: xhat = decode(code) * 2^(exp byte - 127). */
+int orc_attention_mx(const uint16_t* q_lat, const uint16_t* q_rope,
+                     const uint8_t* codes, const uint8_t* exps,
+                     const int64_t* kv_start, const int32_t* kv_len,
+                     int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                     float softmax_scale, int32_t num_splits,
+                     const int64_t* sel, int64_t n_sel, double* out, int threads);
+
 /* Bytes one token occupies per layer: kv_lora + rope code bytes plus the two
  * f32 scales ([colibri#299] PR description: one f32 scale each for Lc, Rc). */
 int64_t orc_bytes_per_token_layer(int32_t kv_lora, int32_t rope);
+
+/* The same for the block-scaled variant: one exponent byte per 32 values. */
+int64_t orc_bytes_per_token_layer_mx(int32_t kv_lora, int32_t rope);
 
 #ifdef __cplusplus
 }

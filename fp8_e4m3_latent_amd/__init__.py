@@ -28,6 +28,7 @@ EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_project_rows
            "kv8_absorb_decode_splitT", "kv8_partials_bytes", "kv8_decode_plan",
            "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
            "kv8_encode_bits", "kv8_decode_codes", "kv8_absorb_decode_noalloc",
+           "kv8_quantize_rows_mx", "kv8_absorb_decode_mx", "kv8_mx_workspace_bytes",
            # include/kv8_pool.h (bound in store.py)
            "kv8_pool_bytes", "kv8_pool_slot_tokens_for", "kv8_store_open", "kv8_store_info",
            "kv8_store_read", "kv8_store_append", "kv8_store_close", "kv8_store_write_f32",
@@ -60,6 +61,8 @@ def lib():
     L.kv8_status_string.argtypes = [ctypes.c_int]
     L.kv8_quantize_rows.restype = ctypes.c_int
     L.kv8_quantize_rows.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+    L.kv8_quantize_rows_mx.restype = ctypes.c_int
+    L.kv8_quantize_rows_mx.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
     L.kv8_project_rows.restype = ctypes.c_int
     L.kv8_project_rows.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, vp, vp]
     L.kv8_norm_rope_quantize_rows.restype = ctypes.c_int
@@ -68,6 +71,10 @@ def lib():
     dec = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
     L.kv8_absorb_decode.restype = ctypes.c_int
     L.kv8_absorb_decode.argtypes = dec + [vp]
+    L.kv8_mx_workspace_bytes.restype = sz
+    L.kv8_mx_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.kv8_absorb_decode_mx.restype = ctypes.c_int
+    L.kv8_absorb_decode_mx.argtypes = dec + [i32, vp, sz, vp]
     L.kv8_absorb_decode_noalloc.restype = ctypes.c_int
     L.kv8_absorb_decode_noalloc.argtypes = dec + [vp]
     L.kv8_splitT_workspace_bytes.restype = sz
@@ -146,6 +153,28 @@ def quantize_rows(src, codes, scales, dst_rows=None, stream=None):
           KV_LORA, ROPE, pc, ps, pd, _stream(stream))
 
 
+def quantize_rows_mx(src, codes, exps, dst_rows=None, stream=None):
+    """Block-scaled quantizer: f32 rows src [n, >=576] -> codes uint8 [rows, 576]
+    and ue8m0 block exponents exps uint8 [rows, 18] (row i -> dst_rows[i] or i)."""
+    torch = _torch()
+    _check(src, "src", torch.float32, 2, contiguous=False)
+    if src.stride(1) != 1 or src.shape[1] < ROW_BYTES:
+        raise ValueError("src rows must be contiguous and hold at least %d values" % ROW_BYTES)
+    pc = _check(codes, "codes", torch.uint8, 2)
+    pe = _check(exps, "exps", torch.uint8, 2)
+    if codes.shape[1] != ROW_BYTES or exps.shape[1] != ROW_BYTES // 32 or exps.shape[0] != codes.shape[0]:
+        raise ValueError("cache must be codes [rows, 576] and exps [rows, 18] uint8")
+    pd = None
+    if dst_rows is not None:
+        pd = _check(dst_rows, "dst_rows", torch.int64, 1)
+        if dst_rows.numel() != src.shape[0]:
+            raise ValueError("dst_rows must have one entry per source row")
+    elif src.shape[0] > codes.shape[0]:
+        raise ValueError("cache has fewer rows than src")
+    _call("kv8_quantize_rows_mx", ctypes.c_void_p(src.data_ptr()), src.stride(0), src.shape[0],
+          KV_LORA, ROPE, pc, pe, pd, _stream(stream))
+
+
 def norm_rope_quantize_rows(src, norm_weight, eps, positions, rope_theta, codes, scales,
                             dst_rows=None, stream=None):
     """The producer step fused with the quantizer: RMS-normalise the Lc part of
@@ -213,7 +242,7 @@ def project_rows(codes, scales, w_kv_b, out=None, rope_out=None, with_rope=True,
     return out, rope_out
 
 
-def _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out):
+def _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out, scales_dtype=None):
     torch = _torch()
     pql = _check(q_lat, "q_lat", torch.bfloat16, 4)
     pqr = _check(q_rope, "q_rope", torch.bfloat16, 4)
@@ -221,7 +250,7 @@ def _decode_args(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len, out):
     if kl != KV_LORA or tuple(q_rope.shape) != (B, Q, H, ROPE):
         raise ValueError("q_lat must be [B,Q,H,512] and q_rope [B,Q,H,64]")
     pc = _check(codes, "codes", torch.uint8, 2)
-    ps = _check(scales, "scales", torch.float32, 2)
+    ps = _check(scales, "scales", scales_dtype or torch.float32, 2)
     pst = _check(kv_start, "kv_start", torch.int64, 1)
     pln = _check(kv_len, "kv_len", torch.int32, 1)
     if kv_start.numel() != B or kv_len.numel() != B:
@@ -273,6 +302,27 @@ def absorb_decode_splitT(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len
     pw = _check(workspace, "workspace", torch.uint8, 1)
     _call("kv8_absorb_decode_splitT", *args, ctypes.c_float(softmax_scale), po,
           int(num_splits), pw, workspace.numel(), _stream(stream))
+    return out
+
+
+def absorb_decode_mx(q_lat, q_rope, codes, exps, kv_start, kv_len, max_len, softmax_scale,
+                     num_splits=1, workspace=None, out=None, stream=None):
+    """Absorbed decode over block-scaled rows (codes uint8 [rows, 576], exps
+    uint8 [rows, 18]); num_splits equal ranges as in absorb_decode_splitT."""
+    torch = _torch()
+    pe = _check(exps, "exps", torch.uint8, 2)
+    if exps.shape[1] != ROW_BYTES // 32 or exps.shape[0] != codes.shape[0]:
+        raise ValueError("exps must be [rows, 18] uint8")
+    args, out, po = _decode_args(q_lat, q_rope, codes, exps.view(torch.uint8), kv_start, kv_len,
+                                 max_len, out, scales_dtype=torch.uint8)
+    args[3] = pe
+    B, Q, H = args[7], args[8], args[9]
+    need = int(lib().kv8_mx_workspace_bytes(B, Q, H, KV_LORA, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    pw = _check(workspace, "workspace", torch.uint8, 1)
+    _call("kv8_absorb_decode_mx", *args, ctypes.c_float(softmax_scale), po, int(num_splits), pw,
+          workspace.numel(), _stream(stream))
     return out
 
 

@@ -47,6 +47,20 @@ int kv8_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows, 
                                               static_cast<hipStream_t>(stream)));
 }
 
+int kv8_quantize_rows_mx(const float* src, int64_t src_row_stride, int64_t n_rows, int32_t kv_lora,
+                         int32_t rope, uint8_t* codes, uint8_t* exps, const int64_t* dst_rows,
+                         void* stream) {
+    if (n_rows < 0) return KV8_EINVAL;
+    if (kv_lora != kv8::kKvLora || rope != kv8::kRope) return KV8_EUNSUPPORTED;
+    if (n_rows == 0) return KV8_OK;
+    if (!src || !codes || !exps) return KV8_EINVAL;
+    if (src_row_stride < kv_lora + rope || src_row_stride % 4 != 0) return KV8_EINVAL;
+    if (!aligned(src, 16) || !aligned(codes, 4)) return KV8_EINVAL;
+    if (dst_rows && !aligned(dst_rows, 8)) return KV8_EINVAL;
+    return launched(kv8::launch_quantize_rows_mx(src, src_row_stride, n_rows, codes, exps, dst_rows,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int kv8_norm_rope_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
                                 int32_t kv_lora, int32_t rope, const float* norm_weight, float eps,
                                 const int64_t* positions, float rope_theta, uint8_t* codes,
@@ -116,9 +130,9 @@ int64_t row_blocks(int32_t Q, int32_t H) {
 }
 
 int check_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,
-                 const float* scales, const int64_t* kv_start, const int32_t* kv_len,
+                 const void* scales, const int64_t* kv_start, const int32_t* kv_len,
                  int32_t max_len, int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
-                 float softmax_scale, const float* out) {
+                 float softmax_scale, const float* out, uintptr_t scales_align = 8) {
     if (B < 1 || Q < 1 || H < 1 || max_len < 0) return KV8_EINVAL;
     if (kv_lora != kv8::kKvLora || rope != kv8::kRope) return KV8_EUNSUPPORTED;
     if (!q_lat || !q_rope || !codes || !scales || !kv_start || !kv_len || !out) return KV8_EINVAL;
@@ -126,7 +140,7 @@ int check_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* c
         softmax_scale == -INFINITY)
         return KV8_EINVAL;
     if (!aligned(q_lat, 16) || !aligned(q_rope, 16) || !aligned(codes, 16) ||
-        !aligned(scales, 8) || !aligned(kv_start, 8) || !aligned(kv_len, 4) || !aligned(out, 16))
+        !aligned(scales, scales_align) || !aligned(kv_start, 8) || !aligned(kv_len, 4) || !aligned(out, 16))
         return KV8_EINVAL;
     const int64_t blocks = static_cast<int64_t>(B) * row_blocks(Q, H);
     // (a sequence's latent query rows must span less than 2^31 bytes: the
@@ -270,6 +284,34 @@ int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8
     rc = launched(kv8::launch_absorb_decode(d, st));
     if (hipFreeAsync(d.workspace, st) != hipSuccess && rc == KV8_OK) rc = KV8_ELAUNCH;
     return rc;
+}
+
+int kv8_absorb_decode_mx(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,
+                         const uint8_t* exps, const int64_t* kv_start, const int32_t* kv_len,
+                         int32_t max_len, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                         int32_t rope, float softmax_scale, float* out, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    // (the exponents take the place of the scales, with byte alignment)
+    int rc = check_decode(q_lat, q_rope, codes, exps, kv_start, kv_len, max_len, B, Q, H, kv_lora,
+                          rope, softmax_scale, out, 1);
+    if (rc != KV8_OK) return rc;
+    if (num_splits < 1 || num_splits > (1 << 20)) return KV8_EINVAL;
+    kv8::DecodeLaunch d =
+        make_launch(q_lat, q_rope, codes, nullptr, kv_start, kv_len, B, Q, H, softmax_scale, out);
+    d.n_sub = sub_splits(B, Q, H, num_splits);
+    d.n_splits = num_splits * d.n_sub;
+    if (d.n_splits > 1) {
+        const size_t need = kv8::mx_workspace_bytes(B, Q, H, d.n_splits);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KV8_EWORKSPACE;
+        d.workspace = workspace;
+    }
+    return launched(kv8::launch_absorb_decode_mx(d, exps, static_cast<hipStream_t>(stream)));
+}
+
+size_t kv8_mx_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t num_splits) {
+    if (B < 1 || Q < 1 || H < 1 || num_splits < 1 || kv_lora != kv8::kKvLora) return 0;
+    const int total = num_splits * sub_splits(B, Q, H, num_splits);
+    return total > 1 ? kv8::mx_workspace_bytes(B, Q, H, total) : 0;
 }
 
 int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,

@@ -19,6 +19,9 @@ int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_r
                                    float theta, uint8_t* codes, float* scales,
                                    const int64_t* dst_rows, hipStream_t stream);
 // encoder 0: the quantizer's conversion; 1: the integer bit-math encoder
+// block-scaled variant: codes [rows][576], ue8m0 exponents [rows][18]
+int launch_quantize_rows_mx(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
+                            uint8_t* exps, const int64_t* dst_rows, hipStream_t stream);
 int launch_encode_bits(uint32_t first, uint64_t count, int encoder, uint8_t* out, hipStream_t stream);
 // non-absorbed projection of cache rows (see kv8_project.hip); N a multiple of 128
 int launch_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
@@ -48,6 +51,11 @@ struct DecodeLaunch {
 size_t splitT_workspace_bytes(int B, int Q, int H, int n_splits);
 // decode kernel (+ merge when n_splits > 1 and `merge` is set)
 int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge = true);
+// the same decode over block-scaled rows (codes + ue8m0 exponents [rows][18]);
+// equal ranges cut into n_sub sub-ranges, n_splits > 1 needs the workspace
+int launch_absorb_decode_mx(const DecodeLaunch& d, const uint8_t* exps, hipStream_t stream);
+// its workspace: f32 partials [n_splits][B][Q*H][512], then 16-byte statistics
+size_t mx_workspace_bytes(int B, int Q, int H, int n_splits);
 int launch_lse_merge(const void* partials, int B, int QH, int n_splits, float softmax_scale,
                      float* out, hipStream_t stream);
 

@@ -275,6 +275,65 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Block-scaled (MX) variant: one power-of-two scale per 32 values (page
+// "Phase 0 toward V4.1 on a 128 GB Mac: lossless mxfp8 residents and
+// kill-test tooling", mxfp8 residents paragraph: e4m3 bytes and ue8m0
+// exponents per 32-wide group).  The block exponent is the smallest E with
+// amax <= 448 * 2^E, read off the bit pattern of amax = m 2^k: 448 = 1.75 *
+// 2^8, so E = k - 8 when m <= 1.75 (mantissa field <= 0x600000) and k - 7
+// otherwise, within [-127, 127]; a zero or subnormal amax gives -127.  Codes
+// are E(x * 2^-E) (an exact power-of-two scaling wherever the code can be
+// nonzero).  Stored as the ue8m0 byte E + 127.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+    const int ef = static_cast<int>(amax_bits >> 23);
+    if (ef == 0) return -127;
+    const int E = ef - 127 - 8 + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+// max over the 8 lanes of each lane octet (every lane gets its octet's maximum)
+__device__ __forceinline__ uint32_t octet_max(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+    return v;
+}
+__device__ __forceinline__ uint32_t encode4_scaled(float4 v, int E) {
+    return encode4_e4m3_hw(__builtin_ldexpf(v.x, -E), __builtin_ldexpf(v.y, -E),
+                           __builtin_ldexpf(v.z, -E), __builtin_ldexpf(v.w, -E));
+}
+
+// One wave quantizes one 576-value row: lane l holds Lc[4l..4l+3],
+// Lc[256+4l..] and (l < 16) Rc[4l..]; octet k of lanes holds block k of each
+// part (Lc blocks k and 8 + k, Rc blocks 16 + k).
+__global__ __launch_bounds__(256) void quantize_rows_mx_kernel(
+    const float* __restrict__ src, int64_t stride, int64_t n_rows, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ exps, const int64_t* __restrict__ dst_rows) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const float* x = src + row * stride;
+    const float4 a = load_stream(x + 4 * lane);
+    const float4 b = load_stream(x + 256 + 4 * lane);
+    float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < 16) c = load_stream(x + kKvLora + 4 * lane);
+    const int Ea = mx_exponent(octet_max(amax4(a)));
+    const int Eb = mx_exponent(octet_max(amax4(b)));
+    const int Ec = mx_exponent(octet_max(amax4(c)));
+    const int64_t d = dst_rows ? dst_rows[row] : row;
+    uint32_t* out = reinterpret_cast<uint32_t*>(codes + d * kRowBytes);
+    __builtin_nontemporal_store(encode4_scaled(a, Ea), out + lane);
+    __builtin_nontemporal_store(encode4_scaled(b, Eb), out + 64 + lane);
+    if (lane < 16) __builtin_nontemporal_store(encode4_scaled(c, Ec), out + kKvLora / 4 + lane);
+    uint8_t* e = exps + d * (kRowBytes / 32);
+    if ((lane & 7) == 0) {
+        e[lane >> 3] = static_cast<uint8_t>(Ea + 127);
+        e[8 + (lane >> 3)] = static_cast<uint8_t>(Eb + 127);
+        if (lane < 16) e[16 + (lane >> 3)] = static_cast<uint8_t>(Ec + 127);
+    }
+}
+
 // out[k] = encode(f32 with bit pattern first + k), 4 codes per thread, with
 // the quantizer's conversion (kBitMath false) or the integer encoder.
 template <bool kBitMath>
@@ -347,6 +406,14 @@ int launch_norm_rope_quantize_rows(const float* src, int64_t stride, int64_t n_r
     for (int i = 0; i < kRope / 2; ++i)
         pa.freq[i] = static_cast<float>(std::pow(static_cast<double>(theta), -2.0 * i / kRope));
     return launch_rows<true>(src, stride, n_rows, codes, scales, dst_rows, pa, stream);
+}
+
+int launch_quantize_rows_mx(const float* src, int64_t stride, int64_t n_rows, uint8_t* codes,
+                            uint8_t* exps, const int64_t* dst_rows, hipStream_t stream) {
+    const int64_t blocks = (n_rows + 3) / 4;
+    hipLaunchKernelGGL(quantize_rows_mx_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                       src, stride, n_rows, codes, exps, dst_rows);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_encode_bits(uint32_t first, uint64_t count, int encoder, uint8_t* out, hipStream_t stream) {

@@ -91,6 +91,24 @@ int kv8_quantize_rows(const float* src, int64_t src_row_stride, int64_t n_rows,
                       uint8_t* codes, float* scales, const int64_t* dst_rows,
                       void* stream);
 
+/* Block-scaled (MX) variant of the quantizer: e4m3 elements with one
+ * power-of-two scale per 32 values instead of one f32 scale per segment (the
+ * e4m3 bytes + ue8m0 exponents of the mxfp8 format on the page "Phase 0
+ * toward V4.1 on a 128 GB Mac: lossless mxfp8 residents and kill-test
+ * tooling" (keep PR #3), mxfp8 residents paragraph): 594 bytes per token and
+ * layer, 8.25 bits per value.
+ *
+ * src, src_row_stride, n_rows, codes, dst_rows   as kv8_quantize_rows.
+ * exps     uint8 [*][(kv_lora + rope) / 32]: block b of cache row r has the
+ *          scale 2^(exps[r][b] - 127) (a ue8m0 byte).
+ * Per block of 32 values: amax over finite entries (0 if none); E = the
+ * smallest integer with amax <= 448 * 2^E, clamped to [-127, 127] (no finite
+ * value saturates); each code is the encoder of kv8_quantize_rows applied to
+ * x * 2^-E.  Results are bit-identical to this definition. */
+int kv8_quantize_rows_mx(const float* src, int64_t src_row_stride, int64_t n_rows,
+                         int32_t kv_lora, int32_t rope, uint8_t* codes, uint8_t* exps,
+                         const int64_t* dst_rows, void* stream);
+
 /* The producer step fused with the quantizer ([colibri#299] commit message,
  * attention_rows item: the producer quantizes the fresh normalised and
  * rotary-embedded latent row in place of the f32 copy).  The page names the
@@ -215,6 +233,29 @@ int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope,
                              float softmax_scale, float* out,
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* Absorbed decode over block-scaled (MX) rows (codes and exponents from
+ * kv8_quantize_rows_mx): the same arguments, ranges, workspace and result as
+ * kv8_absorb_decode_splitT (workspace: kv8_mx_workspace_bytes, which holds
+ * f32 partials), with exps (uint8 [*][(kv_lora + rope) / 32],
+ * block b of row r scaled by 2^(exps[r][b] - 127)) in place of the scales:
+ * s_t = softmax_scale * (q_lat . xhat_Lc[t] + q_rope . xhat_Rc[t]), out =
+ * sum_t softmax(s)_t xhat_Lc[t], xhat = decode(code) * 2^(exp - 127).  The
+ * products are exact (each row's Lc and Rc segments are decoded exactly to
+ * bf16 relative to the segment's largest block; bf16 queries), and the
+ * probabilities enter the context as two bf16 pieces (16 significant bits).
+ * Blocks more than 2^126 below the largest block of their segment are read
+ * as zero.  The kernel reads each token range three times (row maxima, then
+ * the context in two halves of 256 columns). */
+size_t kv8_mx_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
+                              int32_t num_splits);
+int kv8_absorb_decode_mx(const uint16_t* q_lat, const uint16_t* q_rope,
+                         const uint8_t* codes, const uint8_t* exps,
+                         const int64_t* kv_start, const int32_t* kv_len, int32_t max_len,
+                         int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t rope,
+                         float softmax_scale, float* out,
+                         int32_t num_splits, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* ---- Two-stage form of the decode (used by kv8_absorb_decode itself) ----
  * Stage 1 writes one partial softmax per (token range, sequence, query row);

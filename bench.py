@@ -16,19 +16,31 @@ are used in rotation so every step reads its KV from HBM.  Inputs are resident
 in HBM before the timed region; times come from HIP events on the stream the
 kernels run on.  The timed steps have nothing between their kernels; a
 separate pass over the same number of steps, with events between the
-kernels, gives the per-kernel breakdown (`kernel_ms`).  The default 400 untimed steps (about 50 ms) bring the GPU to
-its working clock first: with a handful of warmup steps the timed steps ran
-about 15% slower.  The decode kernel's roofline uses its duration over launches
-of that kernel alone, back to back on the same rotating caches (the per-step
-events around it also hold its dispatch gap behind the append kernel).
+kernels, gives the per-kernel breakdown (`kernel_ms`).  The default 400
+untimed steps (about 50 ms) bring the GPU to its working clock first: with a
+handful of warmup steps the timed steps ran about 15% slower.
 
-Other legs (same JSON line, key "legs"): the bulk quantizer (32,768 tokens x
-61 layers of Student-t rows with planted special rows; the same rows also
-through the producer step fused with the quantizer), the 256k-token
-split-T decode with 64 ranges, and the ragged Q=4 multi-query decode.
+Roofline of the decode kernel: its flops over its mean duration inside the
+steps (HIP events around it on its stream).  Also recorded: the same launches
+back to back (cold: caches in rotation; warm: one cache again and again), the
+shader clock with every SIMD running MFMAs (kv8_shader_clock_mhz; the quoted
+2.5 PFLOP/s assumes 2.4 GHz) and the fraction at that clock, and the HBM
+floor of the kernel's bytes (kv8_stream_floor: one plain streaming launch
+reading a cache copy and writing the partials' bytes).
 
-The CPU baseline is the oracle (oracle/, test infrastructure) timed on a
-bounded sample of the headline decode on this host's cores.
+Other legs (same JSON line, key "legs"): the fp8-vs-f32 gap on the tiny
+workload (B=1, H=16, T=1024: the kernel's output against f32 attention over
+the unquantized rows, computed in f64 with torch on the device), the bulk
+quantizer (32,768 tokens x 61 layers of Student-t rows with planted special
+rows; the same rows also through the producer step fused with the quantizer;
+its HBM floor), the 256k-token split-T decode with 64 ranges, the non-absorbed
+projection, the ragged Q=4 multi-query decode, and the block-scaled (MX)
+variant on the headline shape.  Times are means with medians and bests.
+
+The CPU baseline is the oracle (oracle/, test infrastructure) timed on this
+host: a sample of the headline decode on the host's worker threads and on one
+thread, the quantizer on a slice of the bulk rows, and samples of the 256k and
+ragged workloads (each stated in its "sample").
 """
 import argparse
 import hashlib
@@ -156,55 +168,143 @@ def leg_decode(torch, kv8, W, steps, warmup, cpu_sample_rows):
         "ms_per_step": ms_step,
         "tflops_step": flops / (ms_step * 1e-3) / 1e12,
         "kv_gb_per_s_step": kv_bytes / (ms_step * 1e-3) / 1e9,
+        "step_ms_with_events": spread(iv.sum(axis=1)),
         "kernel_ms": {"quantize_append": float(iv[:, 0].mean()),
                       "absorb_decode_kernel": dec_ms,
                       "lse_merge_kernel": float(iv[:, 2].mean()),
-                      "absorb_decode_kernel_best": float(iv[:, 1].min())},
+                      "absorb_decode_kernel_median": float(np.median(iv[:, 1])),
+                      "absorb_decode_kernel_best": float(iv[:, 1].min()),
+                      "lse_merge_kernel_best": float(iv[:, 2].min())},
         "flops_per_step": flops, "kv_bytes_per_step": kv_bytes,
     }
     # duration of the decode kernel alone for the roofline: the same launches
     # back to back (the per-step events above also hold each launch's
-    # dispatch gap behind the append kernel)
-    b2b = max(steps, 10)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(b2b):
-        c = (warmup + 2 * steps + i) % n_copies
+    # dispatch gap behind the append kernel).  Cold: the three cache copies in
+    # rotation (KV from HBM); warm: one copy again and again (KV in the
+    # last-level cache after the first launch).
+    b2b = 10
+    base = warmup + 2 * steps
+
+    def dec(c):
         kv8.absorb_decode_partials(qs[c][0], qs[c][1], caches[c][0], caches[c][1], kv_start, kv_len,
                                    T, sc, split_tokens, n_splits, partials)
-    e1.record()
-    torch.cuda.synchronize()
-    res["kernel_ms"]["absorb_decode_kernel_back_to_back"] = e0.elapsed_time(e1) / b2b
+
+    res["kernel_ms"]["absorb_decode_kernel_back_to_back"] = back_to_back_ms(
+        torch, b2b, lambda i: dec((base + i) % n_copies))
+    res["kernel_ms"]["absorb_decode_kernel_back_to_back_warm"] = back_to_back_ms(
+        torch, b2b, lambda i: dec(0))
     res["decode_kernel_tflops"] = flops / (dec_ms * 1e-3) / 1e12
     res["decode_kernel_kv_gb_per_s"] = kv_bytes / (dec_ms * 1e-3) / 1e9
-    # CPU baseline: the oracle on a bounded sample of the same decode
+    # the HBM floor of the decode's traffic: one plain streaming launch that
+    # reads a cache copy (codes and scales, copies in rotation) and writes
+    # the partials' bytes
+    rot = iter(range(10 ** 9))
+    part_bytes = partials.numel() * partials.element_size()
+
+    def floor_args():
+        c = next(rot) % n_copies
+        return list(caches[c]), partials
+
+    res["loads_only_floor"] = floor_stats(torch, kv8, 20, floor_args, kv_bytes + part_bytes)
+    # the shader clock under matrix-core load, right after the decode launches
+    res["shader_clock_mhz"] = kv8.shader_clock_mhz(3000)
     cpu = None
     if cpu_sample_rows > 0:
-        import oracle
-        codes, scales = caches[(warmup + steps - 1) % n_copies]
-        c_h, s_h = codes.cpu().numpy(), scales.cpu().numpy()
-        ql_h = qs[(warmup + steps - 1) % n_copies][0].view(torch.int16).cpu().numpy().view(np.uint16)
-        qr_h = qs[(warmup + steps - 1) % n_copies][1].view(torch.int16).cpu().numpy().view(np.uint16)
-        cores = oracle.default_threads()
-        n_sel = min(cpu_sample_rows, B * Q * H)
-        sel = np.linspace(0, B * Q * H - 1, n_sel).astype(np.int64)
-        log("cpu baseline: oracle on %d of %d query rows, %d threads" % (sel.size, B * Q * H, cores))
-        # repeat the sample until about 10 s of CPU work (at most 8 times); median pass
-        times = []
-        while len(times) < 8 and sum(times) < 10.0:
-            t0 = time.perf_counter()
-            oracle.attention(ql_h, qr_h, c_h, s_h, w.kv_start, w.kv_len, Q=Q, softmax_scale=sc,
-                             sel=sel, threads=cores)
-            times.append(time.perf_counter() - t0)
-        dt = float(np.median(times))
-        sflops = float(FLOPS_PER_ROW_TOKEN) * T * sel.size
-        cpu = {"value": sflops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-               "sample": "%d of %d query rows of the headline decode (T=8192, every sequence), "
-                         "f64; median of %d passes, %.2f s each, %.1f s in total"
-                         % (sel.size, B * Q * H, len(times), dt, sum(times))}
+        c = (warmup + steps - 1) % n_copies
+        cpu = cpu_decode_baseline(torch, caches[c], qs[c], w, Q, sc, cpu_sample_rows)
     return res, cpu
+
+
+def _host_bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_passes(fn, budget_s, max_passes=8):
+    """Run fn until about budget_s seconds have passed (at least once); median pass."""
+    times = []
+    while len(times) < max_passes and (not times or sum(times) < budget_s):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), times
+
+
+def cpu_decode_baseline(torch, cache, q, w, Q, sc, sample_rows):
+    """The oracle timed on the headline decode: a sample of query rows on the
+    host's worker threads and a smaller sample on one thread."""
+    import oracle
+    codes, scales = cache
+    c_h, s_h = codes.cpu().numpy(), scales.cpu().numpy()
+    ql_h, qr_h = _host_bits(q[0]), _host_bits(q[1])
+    rows = w.B * Q * w.H
+    T = int(w.kv_len[0])
+    cores = oracle.default_threads()
+    out = {"unit": "TFLOP/s", "kind": "oracle", "cores": cores, "cpu_model": cpu_model(),
+           "host_cpus": os.cpu_count()}
+    for threads, n_sel, budget in ((cores, min(sample_rows, rows), 10.0),
+                                   (1, min(max(sample_rows // 32, 16), rows), 3.0)):
+        sel = np.linspace(0, rows - 1, n_sel).astype(np.int64)
+        log("cpu baseline: oracle on %d of %d query rows, %d threads" % (sel.size, rows, threads))
+        dt, times = _oracle_passes(
+            lambda: oracle.attention(ql_h, qr_h, c_h, s_h, w.kv_start, w.kv_len, Q=Q,
+                                     softmax_scale=sc, sel=sel, threads=threads), budget)
+        v = float(FLOPS_PER_ROW_TOKEN) * T * sel.size / dt / 1e12
+        sample = ("%d of %d query rows of the headline decode (T=%d, every sequence), f64; "
+                  "median of %d passes, %.2f s each" % (sel.size, rows, T, len(times), dt))
+        if threads == cores:
+            out.update({"value": v, "sample": sample})
+        else:
+            out["threads_1"] = {"value": v, "sample": sample}
+    return out
+
+
+def cpu_quantize_baseline(W, cores):
+    """The oracle's quantizer on a slice of the bulk rows (rows/s)."""
+    import oracle
+    rows_h, _ = W.bulk_rows(seed=0, tokens=8192, layers=8)
+    out = {"unit": "rows/s", "kind": "oracle", "cores": cores}
+    for threads, n in ((cores, rows_h.shape[0]), (1, rows_h.shape[0] // 4)):
+        x = np.ascontiguousarray(rows_h[:n])
+        dt, times = _oracle_passes(lambda: oracle.quantize_rows(x, threads=threads), 3.0)
+        key = "value" if threads == cores else "threads_1"
+        rec = {"value": n / dt, "sample": "%d Student-t bulk rows (8,192 tokens x 8 layers, special "
+                                           "rows planted), median of %d passes" % (n, len(times))}
+        if threads == cores:
+            out.update(rec)
+        else:
+            out[key] = rec
+    return out
+
+
+def cpu_workload_baseline(torch, kv8_cache, w, sel, what, cores):
+    """The oracle on the query rows sel of a decode workload (TFLOP/s over the
+    tokens those rows see)."""
+    import oracle
+    codes, scales = kv8_cache
+    c_h, s_h = codes.cpu().numpy(), scales.cpu().numpy()
+    ql, qr = w.q_lat, w.q_rope
+    dt, times = _oracle_passes(
+        lambda: oracle.attention(ql, qr, c_h, s_h, w.kv_start, w.kv_len, Q=w.Q,
+                                 softmax_scale=w.softmax_scale, sel=sel, threads=cores), 4.0, 4)
+    qh = w.Q * w.H
+    seen = 0
+    for r in sel:
+        b, i = int(r) // qh, (int(r) % qh) // w.H
+        seen += max(0, int(w.kv_len[b]) - (w.Q - 1) + i)
+    return {"value": float(FLOPS_PER_ROW_TOKEN) * seen / dt / 1e12, "unit": "TFLOP/s",
+            "kind": "oracle", "cores": cores,
+            "sample": "%s; %d query rows, median of %d passes, %.2f s each" % (what, len(sel), len(times), dt)}
 
 
 def leg_quantize(torch, kv8, W, steps):
@@ -218,15 +318,10 @@ def leg_quantize(torch, kv8, W, steps):
     for _ in range(2):
         kv8.quantize_rows(rows, codes, scales)
     torch.cuda.synchronize()
-    timer = Timer(torch, 2, steps)
-    for t in range(steps):
-        timer.mark(t, 0)
-        kv8.quantize_rows(rows, codes, scales)
-        timer.mark(t, 1)
-    torch.cuda.synchronize()
-    ms = float(timer.intervals_ms()[:, 0].mean())
+    qst = timer_stats(torch, steps, lambda: kv8.quantize_rows(rows, codes, scales))
+    ms = qst["ms"]
     nbytes = float(n) * (4 * D + D + 8)
-    res = {"rows": n, "ms": ms, "rows_per_s": n / (ms * 1e-3),
+    res = {"rows": n, **qst, "rows_per_s": n / (ms * 1e-3),
            "gb_per_s": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes,
            "roofline": roofline_hbm(nbytes, ms, counter_traffic("quantize_rows_kernel",
                                                                 "kv8_quantize.hip"))}
@@ -240,18 +335,24 @@ def leg_quantize(torch, kv8, W, steps):
     for _ in range(2):
         prod()
     torch.cuda.synchronize()
-    pms = timer_call(torch, steps, prod)
+    pst = timer_stats(torch, steps, prod)
+    pms = pst["ms"]
     pbytes = float(n) * (4 * D + 8 + D + 8)
-    res["producer"] = {"rows": n, "ms": pms, "rows_per_s": n / (pms * 1e-3),
+    res["producer"] = {"rows": n, **pst, "rows_per_s": n / (pms * 1e-3),
                        "gb_per_s": pbytes / (pms * 1e-3) / 1e9, "bytes_per_launch": pbytes,
                        "roofline": roofline_hbm(pbytes, pms, counter_traffic("norm_rope_quantize_rows",
                                                                             "kv8_quantize.hip"))}
-    del rows, codes, scales, pos
+    # the HBM floor: one plain streaming launch that reads the source rows and
+    # writes as many bytes as the codes and scales
+    sink = torch.empty(n * (D + 8), dtype=torch.uint8, device="cuda")
+    res["loads_only_floor"] = floor_stats(torch, kv8, steps, lambda: ([rows], sink), nbytes)
+    res["frac_of_floor"] = res["loads_only_floor"]["ms"] / ms
+    del rows, codes, scales, pos, sink
     torch.cuda.empty_cache()
     return res
 
 
-def _decode_workload_leg(torch, kv8, w, steps, splits=None):
+def _decode_workload_leg(torch, kv8, w, steps, splits=None, cpu_sel=None, cpu_what=""):
     dev = "cuda"
     rows = torch.from_numpy(w.rows).to(dev)
     n = w.n_rows
@@ -259,7 +360,8 @@ def _decode_workload_leg(torch, kv8, w, steps, splits=None):
     scales = torch.empty((n, 2), dtype=torch.float32, device=dev)
     kv8.quantize_rows(rows, codes, scales)
     torch.cuda.synchronize()
-    qt = timer_call(torch, steps, lambda: kv8.quantize_rows(rows, codes, scales))
+    qst = timer_stats(torch, steps, lambda: kv8.quantize_rows(rows, codes, scales))
+    qt = qst["ms"]
     del rows
     ql = torch.from_numpy(w.q_lat.view(np.int16)).to(dev).view(torch.bfloat16)
     qr = torch.from_numpy(w.q_rope.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -276,16 +378,90 @@ def _decode_workload_leg(torch, kv8, w, steps, splits=None):
         fn = lambda: kv8.absorb_decode(ql, qr, codes, scales, st, ln, w.max_len, sc, out=out)
     fn()
     torch.cuda.synchronize()
-    ms = timer_call(torch, steps, fn)
+    dst = timer_stats(torch, steps, fn)
+    ms = dst["ms"]
     visible = sum(max(0, int(L) - (w.Q - 1) + i) for L in w.kv_len for i in range(w.Q))
     flops = float(FLOPS_PER_ROW_TOKEN) * w.H * visible
     kv_bytes = float(KV_BYTES_PER_TOKEN) * int(w.kv_len.sum())
     qbytes = float(n) * (4 * D + D + 8)
-    return {"B": w.B, "Q": w.Q, "H": w.H, "tokens": int(w.kv_len.sum()), "ms": ms,
-            "tflops": flops / (ms * 1e-3) / 1e12, "pct_peak_bf16": 100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "kv_gb_per_s": kv_bytes / (ms * 1e-3) / 1e9,
-            "cache_build": {"rows": n, "ms": qt, "rows_per_s": n / (qt * 1e-3),
-                            "gb_per_s": qbytes / (qt * 1e-3) / 1e9}}
+    res = {"B": w.B, "Q": w.Q, "H": w.H, "tokens": int(w.kv_len.sum()), **dst,
+           "tflops": flops / (ms * 1e-3) / 1e12, "pct_peak_bf16": 100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "kv_gb_per_s": kv_bytes / (ms * 1e-3) / 1e9,
+           "cache_build": {"rows": n, **qst, "rows_per_s": n / (qt * 1e-3),
+                           "gb_per_s": qbytes / (qt * 1e-3) / 1e9}}
+    if cpu_sel is not None:
+        import oracle
+        log("cpu baseline: %s" % cpu_what)
+        res["cpu_oracle"] = cpu_workload_baseline(torch, (codes, scales), w, cpu_sel, cpu_what,
+                                                  oracle.default_threads())
+    del codes, scales
+    torch.cuda.empty_cache()
+    return res
+
+
+def leg_mx(torch, kv8, W, steps):
+    """The block-scaled (MX) variant on the headline shape: B=32 x T=8192 x
+    H=128 rows quantized to e4m3 codes with one ue8m0 exponent per 32 values
+    (594 bytes a token), decoded with 8 ranges of 1,024 tokens per sequence
+    (the e4m3 path's plan), plus the MX quantizer over the same rows."""
+    B, T, H, Q = 32, 8192, 128, 1
+    w = W.batched(seed=0, B=B, T=T, H=H)
+    dev = "cuda"
+    rows = torch.from_numpy(w.rows).to(dev)
+    n = B * T
+    codes = torch.empty((n, D), dtype=torch.uint8, device=dev)
+    exps = torch.empty((n, D // 32), dtype=torch.uint8, device=dev)
+    kv8.quantize_rows_mx(rows, codes, exps)
+    torch.cuda.synchronize()
+    qst = timer_stats(torch, steps, lambda: kv8.quantize_rows_mx(rows, codes, exps))
+    del rows
+    ql, qr = W.queries(100, B, Q, H)
+    ql = torch.from_numpy(ql.view(np.int16)).to(dev).view(torch.bfloat16)
+    qr = torch.from_numpy(qr.view(np.int16)).to(dev).view(torch.bfloat16)
+    st = torch.from_numpy(w.kv_start).to(dev)
+    ln = torch.from_numpy(w.kv_len).to(dev)
+    _, splits = kv8.decode_plan(B, Q, H, T)
+    ws = torch.empty(kv8.mx_workspace_bytes(B, Q, H, splits), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Q, H, KL), dtype=torch.float32, device=dev)
+    fn = lambda: kv8.absorb_decode_mx(ql, qr, codes, exps, st, ln, T, float(w.softmax_scale),
+                                      num_splits=splits, workspace=ws, out=out)
+    fn()
+    torch.cuda.synchronize()
+    dst = timer_stats(torch, steps, fn)
+    flops = float(FLOPS_PER_ROW_TOKEN) * B * Q * H * T
+    qbytes = float(n) * (4 * D + D + D // 32)
+    del codes, exps, ws
+    torch.cuda.empty_cache()
+    return {"B": B, "T": T, "H": H, "num_splits": splits, **dst,
+            "tflops": flops / (dst["ms"] * 1e-3) / 1e12,
+            "pct_peak_bf16": 100 * flops / (dst["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "kv_gb_per_s": float(D + D // 32) * n / (dst["ms"] * 1e-3) / 1e9,
+            "quantize": {"rows": n, **qst, "rows_per_s": n / (qst["ms"] * 1e-3),
+                         "gb_per_s": qbytes / (qst["ms"] * 1e-3) / 1e9}}
+
+
+def leg_kv8_gap(torch, kv8, W):
+    """The tiny workload (B=1, H=16, T=1024, 1% outliers x50) decoded from the
+    fp8 cache against f32 attention over the unquantized rows, in f64 with
+    plain torch on the device: the difference the fp8 cache makes (the
+    KV8=1 vs KV8=0 comparison), max|d| / max|ref|."""
+    w = W.tiny(seed=0)
+    dev = "cuda"
+    rows = torch.from_numpy(w.rows).to(dev)
+    codes = torch.empty((w.n_rows, D), dtype=torch.uint8, device=dev)
+    scales = torch.empty((w.n_rows, 2), dtype=torch.float32, device=dev)
+    kv8.quantize_rows(rows, codes, scales)
+    ql = torch.from_numpy(w.q_lat.view(np.int16)).to(dev).view(torch.bfloat16)
+    qr = torch.from_numpy(w.q_rope.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = kv8.absorb_decode(ql, qr, codes, scales, torch.from_numpy(w.kv_start).to(dev),
+                            torch.from_numpy(w.kv_len).to(dev), w.max_len, float(w.softmax_scale))
+    x = rows.double()
+    s = (ql.double().reshape(-1, KL) @ x[:, :KL].T.contiguous()
+         + qr.double().reshape(-1, KR) @ x[:, KL:].T.contiguous())
+    p = torch.softmax(s * float(w.softmax_scale), dim=1)
+    ref = p @ x[:, :KL]
+    d = (out.double().reshape(-1, KL) - ref).abs().max() / ref.abs().max()
+    return {"workload": "tiny: B=1, H=16, T=1024, rows N(0,1) with 1% of entries x50", "max_abs_rel": float(d)}
 
 
 def leg_project(torch, kv8, steps):
@@ -332,13 +508,47 @@ def leg_copy(torch, steps):
 
 
 def timer_call(torch, steps, fn):
+    """Mean ms of fn over steps launches, each bracketed by HIP events."""
+    return timer_stats(torch, steps, fn)["ms"]
+
+
+def timer_stats(torch, steps, fn):
     timer = Timer(torch, 2, steps)
     for t in range(steps):
         timer.mark(t, 0)
         fn()
         timer.mark(t, 1)
     torch.cuda.synchronize()
-    return float(timer.intervals_ms()[:, 0].mean())
+    return spread(timer.intervals_ms()[:, 0])
+
+
+def spread(ms):
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"ms": float(ms.mean()), "ms_median": float(np.median(ms)), "ms_best": float(ms.min())}
+
+
+def back_to_back_ms(torch, n, fn):
+    """Mean ms per launch of n launches of fn(i) with nothing between them."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def floor_stats(torch, kv8, steps, fn_reads_write, nbytes):
+    """Time kv8_stream_floor over the same bytes as a kernel: fn_reads_write(i)
+    returns (reads, write) for launch i."""
+    fn = lambda: kv8.stream_floor(*fn_reads_write())
+    fn()
+    st = timer_stats(torch, steps, fn)
+    st["bytes"] = nbytes
+    st["gb_per_s"] = nbytes / (st["ms"] * 1e-3) / 1e9
+    return st
 
 
 def roofline_hbm(nbytes, ms, traffic):
@@ -352,8 +562,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--legs", default="decode,quantize,splitT,project,ragged",
-                    help="comma list of decode, quantize, splitT, project, ragged, copy")
+    ap.add_argument("--legs", default="decode,quantize,splitT,project,ragged,mx",
+                    help="comma list of quantize, splitT, project, ragged, mx, copy "
+                         "(the headline decode always runs)")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096,
                     help="query rows the oracle times for the CPU baseline (0: skip)")
     args = ap.parse_args()
@@ -374,19 +585,32 @@ def main():
 
     res, cpu = leg_decode(torch, kv8, W, args.steps, args.warmup, args.cpu_sample_rows)
     flops = res["flops_per_step"]
-    dec_ms = res["kernel_ms"]["absorb_decode_kernel_back_to_back"]
+    # the decode kernel's mean duration inside the steps (HIP events around it)
+    dec_ms = res["kernel_ms"]["absorb_decode_kernel"]
     ach = flops / (dec_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": "absorb_decode_kernel", "kernel_ms": dec_ms,
             "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": ach / PEAK_BF16_TFLOPS,
             "traffic": counter_traffic("absorb_decode_kernel", "kv8_decode.hip")}
-    extra = {}
+    clock = res["shader_clock_mhz"]
+    roof["shader_clock_mhz"] = clock
+    # the same peak at the clock the matrix cores ran at (the quoted peak
+    # assumes the 2.4 GHz peak engine clock)
+    roof["frac_at_measured_clock"] = ach / (PEAK_BF16_TFLOPS * clock / 2400.0)
+    cpu_on = args.cpu_sample_rows > 0
+    extra = {"kv8_gap_tiny": leg_kv8_gap(torch, kv8, W)}
     if "quantize" in legs:
         extra["bulk_quantize"] = leg_quantize(torch, kv8, W, max(5, args.steps // 2))
+        if cpu_on:
+            import oracle
+            log("cpu baseline: oracle quantizer")
+            cpu["quantize"] = cpu_quantize_baseline(W, oracle.default_threads())
     if "splitT" in legs:
         log("splitT: 256k-token slot, 64 ranges")
-        extra["splitT_256k"] = _decode_workload_leg(torch, kv8, W.long_context(seed=0),
-                                                    max(5, args.steps // 2), splits=64)
+        sel = np.arange(0, 128, 8) if cpu_on else None
+        extra["splitT_256k"] = _decode_workload_leg(
+            torch, kv8, W.long_context(seed=0), max(5, args.steps // 2), splits=64, cpu_sel=sel,
+            cpu_what="256k-token slot, every 8th of the 128 heads (16 rows), T=262,144")
     if "project" in legs:
         log("project: 8192 rows x N=32768")
         extra["project_8k"] = leg_project(torch, kv8, max(5, args.steps // 4))
@@ -394,8 +618,15 @@ def main():
         extra["copy_1gib"] = leg_copy(torch, 3)
     if "ragged" in legs:
         log("ragged: B=64, lengths U[1k,64k], Q=4")
-        extra["ragged_q4"] = _decode_workload_leg(torch, kv8, W.ragged(seed=0),
-                                                  max(3, args.steps // 4))
+        # CPU subset: the first 8 sequences, all 4 query positions, every 16th head
+        sel = (np.array([b * 512 + q * 128 + h for b in range(8) for q in range(4)
+                         for h in range(0, 128, 16)]) if cpu_on else None)
+        extra["ragged_q4"] = _decode_workload_leg(
+            torch, kv8, W.ragged(seed=0), max(3, args.steps // 4), cpu_sel=sel,
+            cpu_what="ragged Q=4: sequences 0-7, every query position, every 16th head")
+    if "mx" in legs:
+        log("mx: block-scaled variant, B=32 x T=8192 x H=128")
+        extra["mx_decode"] = leg_mx(torch, kv8, W, max(5, args.steps // 4))
     line = {
         "metric": METRIC,
         "value": res["tflops_step"],
@@ -417,6 +648,8 @@ def main():
         "pct_peak_bf16": 100 * res["tflops_step"] / PEAK_BF16_TFLOPS,
         "kv_gb_per_s": res["kv_gb_per_s_step"],
         "kernel_ms": res["kernel_ms"],
+        "step_ms_with_events": res["step_ms_with_events"],
+        "decode_loads_only_floor": res["loads_only_floor"],
         "roofline": roof,
         "cpu_baseline": cpu,
         "legs": extra,

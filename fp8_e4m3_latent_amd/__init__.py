@@ -29,6 +29,7 @@ EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_project_rows
            "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
            "kv8_encode_bits", "kv8_decode_codes", "kv8_absorb_decode_noalloc",
            "kv8_quantize_rows_mx", "kv8_absorb_decode_mx", "kv8_mx_workspace_bytes",
+           "kv8_shader_clock_mhz", "kv8_stream_floor",
            # include/kv8_pool.h (bound in store.py)
            "kv8_pool_bytes", "kv8_pool_slot_tokens_for", "kv8_store_open", "kv8_store_info",
            "kv8_store_read", "kv8_store_append", "kv8_store_close", "kv8_store_write_f32",
@@ -57,6 +58,10 @@ def lib():
     vp, i32, i64, u32, u64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                        ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t,
                                        ctypes.c_float)
+    L.kv8_stream_floor.restype = ctypes.c_int
+    L.kv8_stream_floor.argtypes = [vp, u64, vp, u64, vp, u64, vp]
+    L.kv8_shader_clock_mhz.restype = ctypes.c_int
+    L.kv8_shader_clock_mhz.argtypes = [i32, ctypes.POINTER(ctypes.c_double), vp]
     L.kv8_status_string.restype = ctypes.c_char_p
     L.kv8_status_string.argtypes = [ctypes.c_int]
     L.kv8_quantize_rows.restype = ctypes.c_int
@@ -326,6 +331,10 @@ def absorb_decode_mx(q_lat, q_rope, codes, exps, kv_start, kv_len, max_len, soft
     return out
 
 
+def mx_workspace_bytes(B, Q, H, num_splits):
+    return int(lib().kv8_mx_workspace_bytes(B, Q, H, KV_LORA, num_splits))
+
+
 def decode_plan(B, Q, H, max_len):
     """(split_tokens, num_splits) that absorb_decode uses for these shapes."""
     a, n = ctypes.c_int32(), ctypes.c_int32()
@@ -381,3 +390,22 @@ def decode_codes(codes, stream=None):
     _call("kv8_decode_codes", pc, codes.numel(), ctypes.c_void_p(bf.data_ptr()),
           ctypes.c_void_p(hf.data_ptr()), _stream(stream))
     return bf, hf
+
+
+def shader_clock_mhz(busy_us=2000, stream=None):
+    """Shader clock (MHz) of the current device with every SIMD running fp16
+    MFMAs for about busy_us microseconds (synchronizes the stream)."""
+    v = ctypes.c_double()
+    _call("kv8_shader_clock_mhz", busy_us, ctypes.byref(v), _stream(stream))
+    return v.value
+
+
+def stream_floor(reads, write=None, stream=None):
+    """One launch reading up to two device tensors and writing `write` (its
+    content is overwritten) with plain 16-byte streaming loads and stores:
+    the HBM floor for a kernel moving the same bytes."""
+    ptrs = []
+    for t in list(reads) + [None] * (2 - len(reads)):
+        ptrs += [None, 0] if t is None else [ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size()]
+    wp, wb = (None, 0) if write is None else (ctypes.c_void_p(write.data_ptr()), write.numel() * write.element_size())
+    _call("kv8_stream_floor", *ptrs, wp, wb, _stream(stream))

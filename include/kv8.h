@@ -352,6 +352,25 @@ int kv8_encode_bits(uint32_t first, uint64_t count, int32_t encoder, uint8_t* ou
 int kv8_decode_codes(const uint8_t* codes, int64_t n, uint16_t* out_bf16, uint16_t* out_f16,
                      void* stream);
 
+/* ---- Measurement ---- */
+
+/* The shader clock, in MHz, of the current device while every SIMD runs a
+ * chain of fp16 MFMAs for about busy_us microseconds (1..100000): the median
+ * over blocks of (shader-clock counter delta / wall-clock counter delta) times
+ * the wall clock's rate.  MI355X's dense MFMA peaks are quoted at its 2.4 GHz
+ * peak engine clock; this is the clock matrix-core-bound kernels actually get.
+ * Allocates and frees a small device buffer, synchronizes the stream.
+ * KV8_EINVAL for a bad argument, KV8_ENOMEM, KV8_ELAUNCH. */
+int kv8_shader_clock_mhz(int32_t busy_us, double* mhz, void* stream);
+
+/* HBM floor of a kernel's traffic: one launch that reads bytes0 at src0 and
+ * bytes1 at src1 and writes dst_bytes at dst (content unspecified) with plain
+ * 16-byte grid-stride loads and stores, nothing else.  Sizes multiples of 16,
+ * pointers 16-byte aligned when their size is non-zero (else KV8_EINVAL).
+ * Asynchronous on stream; KV8_ELAUNCH when the launch fails. */
+int kv8_stream_floor(const void* src0, uint64_t bytes0, const void* src1, uint64_t bytes1,
+                     void* dst, uint64_t dst_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

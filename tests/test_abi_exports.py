@@ -122,3 +122,19 @@ def test_two_stage_calls_check_sizes_before_any_gpu_work():
     # too small a buffer for the ranges asked for
     assert part(*args, 4000, 2, 1, 128, 512, 64, f32(0.04), 1024, 4, fake,
                 L.kv8_partials_bytes(2, 1, 128, 512, 3), None) == -4
+
+
+def test_measurement_entry_points_reject_bad_arguments_before_any_gpu_work():
+    if not os.path.exists(kv8.LIB_PATH):
+        pytest.skip("libkv8.so not built")
+    L = kv8.lib()
+    mhz = ctypes.c_double()
+    assert L.kv8_shader_clock_mhz(0, ctypes.byref(mhz), None) == -1
+    assert L.kv8_shader_clock_mhz(100001, ctypes.byref(mhz), None) == -1
+    assert L.kv8_shader_clock_mhz(1000, None, None) == -1
+    # sizes must be multiples of 16 and non-empty ranges need aligned pointers
+    assert L.kv8_stream_floor(None, 8, None, 0, None, 0, None) == -1
+    assert L.kv8_stream_floor(None, 16, None, 0, None, 0, None) == -1
+    assert L.kv8_stream_floor(ctypes.c_void_p(0x1008), 16, None, 0, None, 0, None) == -1
+    assert L.kv8_stream_floor(None, 0, None, 0, ctypes.c_void_p(0x1000), 24, None) == -1
+    assert L.kv8_stream_floor(None, 0, None, 0, None, 0, None) == 0

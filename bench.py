@@ -466,7 +466,8 @@ def leg_kv8_gap(torch, kv8, W):
 
 def leg_project(torch, kv8, steps):
     """Non-absorbed projection of one 8,192-token sequence's cache rows by a
-    bf16 kv_b weight of N = 128 heads x (128 + 128) columns (random weights)."""
+    bf16 kv_b weight of N = 128 heads x (128 + 128) columns (random weights),
+    with bf16 output and with f32 output."""
     n, N = 8192, 32768
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
@@ -476,21 +477,30 @@ def leg_project(torch, kv8, steps):
     kv8.quantize_rows(rows, codes, scales)
     del rows
     w = (torch.randn((N, KL), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
-    out = torch.empty((n, N), dtype=torch.bfloat16, device="cuda")
     rope = torch.empty((n, KR), dtype=torch.float32, device="cuda")
-    fn = lambda: kv8.project_rows(codes, scales, w, out=out, rope_out=rope)
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
-    ms = timer_call(torch, steps, fn)
     flops = 2.0 * n * KL * N
-    nbytes = float(n) * (D + 8) + 2.0 * N * KL + 2.0 * n * N + 4.0 * n * KR
-    ach = flops / (ms * 1e-3) / 1e12
-    del codes, scales, w, out, rope
+    res = {"rows": n, "N": N}
+    for name, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        out = torch.empty((n, N), dtype=dt, device="cuda")
+        fn = lambda: kv8.project_rows(codes, scales, w, out=out, rope_out=rope)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        st = timer_stats(torch, steps, fn)
+        ms = st["ms"]
+        nbytes = float(n) * (D + 8) + 2.0 * N * KL + out.element_size() * float(n) * N + 4.0 * n * KR
+        ach = flops / (ms * 1e-3) / 1e12
+        rec = {**st, "tflops": ach, "gb_per_s": nbytes / (ms * 1e-3) / 1e9,
+               "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}}
+        if name == "bf16":
+            res.update(rec)
+        else:
+            res["f32_out"] = rec
+        del out
+    del codes, scales, w, rope
     torch.cuda.empty_cache()
-    return {"rows": n, "N": N, "ms": ms, "tflops": ach, "gb_per_s": nbytes / (ms * 1e-3) / 1e9,
-            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}}
+    return res
 
 
 def leg_copy(torch, steps):

@@ -24,7 +24,7 @@ _STATUS = {0: "KV8_OK", -1: "KV8_EINVAL", -2: "KV8_EUNSUPPORTED", -3: "KV8_ELAUN
            -4: "KV8_EWORKSPACE", -5: "KV8_ENOMEM", -6: "KV8_EIO", -7: "KV8_EFORMAT"}
 
 # every symbol include/kv8.h declares
-EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_project_rows", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
+EXPORTS = ("kv8_quantize_rows", "kv8_norm_rope_quantize_rows", "kv8_project_rows", "kv8_project_rows_f32", "kv8_absorb_decode", "kv8_splitT_workspace_bytes",
            "kv8_absorb_decode_splitT", "kv8_partials_bytes", "kv8_decode_plan",
            "kv8_absorb_decode_partials", "kv8_lse_merge", "kv8_status_string",
            "kv8_encode_bits", "kv8_decode_codes", "kv8_absorb_decode_noalloc",
@@ -70,6 +70,8 @@ def lib():
     L.kv8_quantize_rows_mx.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
     L.kv8_project_rows.restype = ctypes.c_int
     L.kv8_project_rows.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, vp, vp]
+    L.kv8_project_rows_f32.restype = ctypes.c_int
+    L.kv8_project_rows_f32.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, vp, vp]
     L.kv8_norm_rope_quantize_rows.restype = ctypes.c_int
     L.kv8_norm_rope_quantize_rows.argtypes = [vp, i64, i64, i32, i32, vp, f32, vp, f32, vp, vp,
                                               vp, vp]
@@ -214,10 +216,12 @@ def norm_rope_quantize_rows(src, norm_weight, eps, positions, rope_theta, codes,
           _stream(stream))
 
 
-def project_rows(codes, scales, w_kv_b, out=None, rope_out=None, with_rope=True, stream=None):
+def project_rows(codes, scales, w_kv_b, out=None, rope_out=None, with_rope=True, out_dtype=None,
+                 stream=None):
     """Non-absorbed projection of the cache rows codes [n, 576] / scales [n, 2]
-    (a contiguous slice of the cache): out bf16 [n, N] = s_Lc * dec(Lc) @ W^T
-    for the bf16 weight w_kv_b [N, 512]; rope_out f32 [n, 64] = s_Rc * dec(Rc).
+    (a contiguous slice of the cache): out [n, N] = s_Lc * dec(Lc) @ W^T for
+    the bf16 weight w_kv_b [N, 512], in bf16 (default) or f32 (out_dtype, or
+    the dtype of a given out); rope_out f32 [n, 64] = s_Rc * dec(Rc).
     Returns (out, rope_out) (rope_out None when with_rope is False)."""
     torch = _torch()
     pc = _check(codes, "codes", torch.uint8, 2)
@@ -230,8 +234,9 @@ def project_rows(codes, scales, w_kv_b, out=None, rope_out=None, with_rope=True,
     if w_kv_b.shape[1] != KV_LORA:
         raise ValueError("w_kv_b must be [N, 512]")
     if out is None:
-        out = torch.empty((n, N), dtype=torch.bfloat16, device=codes.device)
-    po = _check(out, "out", torch.bfloat16, 2)
+        out = torch.empty((n, N), dtype=out_dtype or torch.bfloat16, device=codes.device)
+    f32 = out.dtype == torch.float32
+    po = _check(out, "out", torch.float32 if f32 else torch.bfloat16, 2)
     if tuple(out.shape) != (n, N):
         raise ValueError("out must be [n, N]")
     pr = None
@@ -243,7 +248,8 @@ def project_rows(codes, scales, w_kv_b, out=None, rope_out=None, with_rope=True,
             raise ValueError("rope_out must be [n, 64]")
     else:
         rope_out = None
-    _call("kv8_project_rows", pc, ps, n, KV_LORA, ROPE, pw, N, po, pr, _stream(stream))
+    _call("kv8_project_rows_f32" if f32 else "kv8_project_rows", pc, ps, n, KV_LORA, ROPE, pw, N, po, pr,
+          _stream(stream))
     return out, rope_out
 
 

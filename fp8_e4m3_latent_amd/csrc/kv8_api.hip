@@ -81,9 +81,9 @@ int kv8_norm_rope_quantize_rows(const float* src, int64_t src_row_stride, int64_
                                                         static_cast<hipStream_t>(stream)));
 }
 
-int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, int32_t kv_lora,
-                     int32_t rope, const uint16_t* w_kv_b, int32_t N, uint16_t* out,
-                     float* rope_out, void* stream) {
+static int project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, int32_t kv_lora,
+                        int32_t rope, const uint16_t* w_kv_b, int32_t N, void* out, bool out_f32,
+                        float* rope_out, void* stream) {
     if (n_rows < 0 || N < 0) return KV8_EINVAL;
     if (kv_lora != kv8::kKvLora || rope != kv8::kRope) return KV8_EUNSUPPORTED;
     if (N % 128 != 0) return KV8_EUNSUPPORTED;
@@ -92,9 +92,21 @@ int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, 
     if (!aligned(codes, 16) || !aligned(scales, 8) || !aligned(w_kv_b, 16) || !aligned(out, 16) ||
         (rope_out && !aligned(rope_out, 16)))
         return KV8_EINVAL;
-    if ((n_rows + 127) / 128 * (N / 128) > (int64_t(1) << 31) - 1) return KV8_EUNSUPPORTED;
-    return launched(kv8::launch_project_rows(codes, scales, n_rows, w_kv_b, N, out, rope_out,
+    if ((n_rows + 255) / 256 * ((N + 255) / 256) > (int64_t(1) << 31) - 1) return KV8_EUNSUPPORTED;
+    return launched(kv8::launch_project_rows(codes, scales, n_rows, w_kv_b, N, out, out_f32, rope_out,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, int32_t kv_lora,
+                     int32_t rope, const uint16_t* w_kv_b, int32_t N, uint16_t* out,
+                     float* rope_out, void* stream) {
+    return project_rows(codes, scales, n_rows, kv_lora, rope, w_kv_b, N, out, false, rope_out, stream);
+}
+
+int kv8_project_rows_f32(const uint8_t* codes, const float* scales, int64_t n_rows, int32_t kv_lora,
+                         int32_t rope, const uint16_t* w_kv_b, int32_t N, float* out,
+                         float* rope_out, void* stream) {
+    return project_rows(codes, scales, n_rows, kv_lora, rope, w_kv_b, N, out, true, rope_out, stream);
 }
 
 int kv8_encode_bits(uint32_t first, uint64_t count, int32_t encoder, uint8_t* out, void* stream) {

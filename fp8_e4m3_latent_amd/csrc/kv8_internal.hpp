@@ -25,7 +25,7 @@ int launch_quantize_rows_mx(const float* src, int64_t stride, int64_t n_rows, ui
 int launch_encode_bits(uint32_t first, uint64_t count, int encoder, uint8_t* out, hipStream_t stream);
 // non-absorbed projection of cache rows (see kv8_project.hip); N a multiple of 128
 int launch_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
-                        const uint16_t* w_kv_b, int N, uint16_t* out, float* rope_out,
+                        const uint16_t* w_kv_b, int N, void* out, bool out_f32, float* rope_out,
                         hipStream_t stream);
 // One absorbed-decode launch (see kv8_decode.hip).  Token ranges: with
 // split_chunk > 0 range s of a sequence is [s * split_chunk, (s+1) * split_chunk);

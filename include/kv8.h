@@ -333,6 +333,15 @@ int kv8_project_rows(const uint8_t* codes, const float* scales, int64_t n_rows, 
                      int32_t rope, const uint16_t* w_kv_b, int32_t N, uint16_t* out,
                      float* rope_out, void* stream);
 
+/* kv8_project_rows with f32 output, the f32 staging the page's kv_b matmul
+ * takes: out[m][n] = s_Lc[m] * sum_k decode(codes[m][k]) * W[n][k], the f32
+ * sum of the exact bf16 products times the row scale, not rounded further.
+ * out f32 [n_rows][N], 16-byte aligned; every other argument, the rope
+ * output and the status codes as kv8_project_rows. */
+int kv8_project_rows_f32(const uint8_t* codes, const float* scales, int64_t n_rows, int32_t kv_lora,
+                         int32_t rope, const uint16_t* w_kv_b, int32_t N, float* out,
+                         float* rope_out, void* stream);
+
 /* Human-readable name of a kv8_status value (static string, never NULL). */
 const char* kv8_status_string(int status);
 

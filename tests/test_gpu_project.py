@@ -5,11 +5,12 @@ Page: "KV8=1: fp8 e4m3 latent KV cache (CPU + CUDA) with .coli_kv v2"
 (colibri PR #299), commit message, attention_rows item.
 
 The kernel sums bf16 x bf16 products in f32 (every e4m3 value is exact in
-bf16) and rounds the scaled sum to bf16; the oracle sums in f64.  Bar per
-element: |gpu - ref| <= 2^-8 |ref| + 2^-20 s_Lc sum_k |dec(c_k)| |W_nk| (one bf16
-rounding plus the f32 accumulation of 512 products).  The dequantized Rc
-(one f32 product of exact values) must equal the oracle's value rounded to
-f32, bit for bit.
+bf16) and scales the sum; the oracle sums in f64.  Bar per element: |gpu - ref|
+<= e |ref| + 2^-20 s_Lc sum_k |dec(c_k)| |W_nk|, e = 2^-8 for the bf16 output
+(one rounding to bf16) and 2^-23 for the f32 output (the rounding of the
+scale's product), plus the f32 accumulation of 512 exact products.  The
+dequantized Rc (one f32 product of exact values) must equal the oracle's
+value rounded to f32, bit for bit.
 """
 import numpy as np
 import pytest
@@ -59,7 +60,8 @@ def check(c, s, wbits, rows, got, got_rope):
     g = got.float().cpu().numpy().astype(np.float64)[rows] if got.shape[0] != len(rows) else got.float().cpu().numpy().astype(np.float64)
     x = np.abs(oracle.decode(c[rows, :KL])) * s[rows, :1].astype(np.float64)
     wv = np.abs((wbits.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
-    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -20 * (x @ wv.T)
+    e = 2.0 ** -23 if got.dtype == torch.float32 else 2.0 ** -8
+    bound = e * np.abs(ref) + 2.0 ** -20 * (x @ wv.T)
     err = np.abs(g - ref)
     assert np.all(err <= bound), "max err/bound %.3f" % float(np.max(err / np.maximum(bound, 1e-300)))
     if got_rope is not None:
@@ -69,13 +71,16 @@ def check(c, s, wbits, rows, got, got_rope):
     return float(np.max(err / np.maximum(np.abs(ref).max(), 1e-300)))
 
 
-@pytest.mark.parametrize("n,N", [(1, 128), (100, 256), (300, 384), (1000, 128)])
-def test_project_small(kv8, n, N):
-    """Row counts below, at and across the 128-row tile, several column tiles."""
-    say("project: n=%d N=%d" % (n, N))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,N", [(1, 128), (100, 256), (300, 384), (1000, 128), (513, 640)])
+def test_project_small(kv8, n, N, dtype):
+    """Row counts below, at and across the 256-row tile, several column tiles
+    (N = 128 and 384 end in half a column tile)."""
+    say("project: n=%d N=%d %s" % (n, N, dtype))
     codes, scales, c, s = gpu_cache(kv8, n, 40 + n)
     wb, wbits = weights(N, 41 + N)
-    out, rope = kv8.project_rows(codes, scales, wb)
+    out, rope = kv8.project_rows(codes, scales, wb,
+                                 out_dtype=torch.float32 if dtype == "f32" else torch.bfloat16)
     torch.cuda.synchronize()
     e = check(c, s, wbits, np.arange(n), out, rope)
     say("  max |err| / max |ref| = %.2e" % e)
@@ -91,15 +96,17 @@ def test_project_slice_of_cache_and_no_rope(kv8):
     check(c[200:530], s[200:530], wbits, np.arange(330), out, None)
 
 
-def test_project_full_size(kv8):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_project_full_size(kv8, dtype):
     """8,192 rows (one 8k-token sequence) x N = 32,768 (128 heads x (128 + 128)):
-    every row of the first 128-column tile set, and 48 sampled rows over every
+    every row of the first 128 columns, and 48 sampled rows over every
     column."""
     n, N = 8192, 32768
-    say("project: full size n=%d N=%d" % (n, N))
+    say("project: full size n=%d N=%d %s" % (n, N, dtype))
     codes, scales, c, s = gpu_cache(kv8, n, 52)
     wb, wbits = weights(N, 53)
-    out, rope = kv8.project_rows(codes, scales, wb)
+    out, rope = kv8.project_rows(codes, scales, wb,
+                                 out_dtype=torch.float32 if dtype == "f32" else torch.bfloat16)
     torch.cuda.synchronize()
     e0 = check(c, s, wbits[:128], np.arange(n), out[:, :128], rope)
     say("  columns 0..127, every row: max |err| / max |ref| = %.2e" % e0)

@@ -193,6 +193,22 @@ def leg_decode(torch, kv8, W, steps, warmup, cpu_sample_rows):
         torch, b2b, lambda i: dec((base + i) % n_copies))
     res["kernel_ms"]["absorb_decode_kernel_back_to_back_warm"] = back_to_back_ms(
         torch, b2b, lambda i: dec(0))
+    # the one-call entry point, which takes stream-ordered memory for its
+    # partials on every call, against the same decode and merge on a
+    # caller-owned partials buffer
+    out1 = torch.empty_like(out)
+
+    def one_call(i):
+        c = (base + i) % n_copies
+        kv8.absorb_decode(qs[c][0], qs[c][1], caches[c][0], caches[c][1], kv_start, kv_len, T, sc, out=out1)
+
+    def two_stage(i):
+        dec((base + i) % n_copies)
+        kv8.lse_merge(partials, B, Q, H, n_splits, sc, out1)
+
+    one_call(0)
+    res["kernel_ms"]["absorb_decode_call_allocating"] = back_to_back_ms(torch, b2b, one_call)
+    res["kernel_ms"]["absorb_decode_partials_plus_merge"] = back_to_back_ms(torch, b2b, two_stage)
     res["decode_kernel_tflops"] = flops / (dec_ms * 1e-3) / 1e12
     res["decode_kernel_kv_gb_per_s"] = kv_bytes / (dec_ms * 1e-3) / 1e9
     # the HBM floor of the decode's traffic: one plain streaming launch that

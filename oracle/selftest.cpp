@@ -105,6 +105,23 @@ int main() {
     std::vector<double> po(static_cast<size_t>(n) * N), pr(static_cast<size_t>(n) * KR);
     orc_project_rows(codes.data(), scales.data(), n, KL, KR, wb.data(), N, po.data(), pr.data(), 3);
     CHECK(po[static_cast<size_t>(1) * N] == 0.0 && pr[static_cast<size_t>(1) * KR] == 0.0);  // zero row
+
+    // block-scaled variant: the same special rows, scattered; attention over them
+    const int NB = D / 32;
+    std::vector<uint8_t> mcodes(static_cast<size_t>(2 * n) * D, 0xAA);
+    std::vector<uint8_t> mexps(static_cast<size_t>(2 * n) * NB, 0xCD);
+    orc_quantize_rows_mx(rows.data(), D, n, KL, KR, mcodes.data(), mexps.data(), dst.data(), 3);
+    CHECK(mexps[static_cast<size_t>(3) * NB] == 0);                  // zero block: E = -127
+    CHECK(mcodes[static_cast<size_t>(7) * D + 5] == 0);              // NaN -> 0
+    CHECK(mcodes[static_cast<size_t>(9) * D + 7] == 0x7E + 0x80);    // -inf saturates
+    std::vector<double> mout(static_cast<size_t>(2) * KL);
+    const int64_t mstart[1] = {1};
+    const int32_t mlen[1] = {2 * n - 1};
+    CHECK(orc_attention_mx(ql.data(), qr.data(), mcodes.data(), mexps.data(), mstart, mlen, 1, 1, 2, KL, KR,
+                           1.0f / 24.0f, 3, nullptr, 0, mout.data(), 2) == 0);
+    for (double v : mout) CHECK(std::isfinite(v));
+    CHECK(orc_bytes_per_token_layer_mx(KL, KR) == D + NB);
+
     std::printf("oracle selftest ok\n");
     return 0;
 }

@@ -319,7 +319,8 @@ def absorb_decode_splitT(q_lat, q_rope, codes, scales, kv_start, kv_len, max_len
 def absorb_decode_mx(q_lat, q_rope, codes, exps, kv_start, kv_len, max_len, softmax_scale,
                      num_splits=1, workspace=None, out=None, stream=None):
     """Absorbed decode over block-scaled rows (codes uint8 [rows, 576], exps
-    uint8 [rows, 18]); num_splits equal ranges as in absorb_decode_splitT."""
+    uint8 [rows, 18], 4-byte aligned); num_splits equal ranges as in
+    absorb_decode_splitT."""
     torch = _torch()
     pe = _check(exps, "exps", torch.uint8, 2)
     if exps.shape[1] != ROW_BYTES // 32 or exps.shape[0] != codes.shape[0]:

@@ -303,27 +303,28 @@ int kv8_absorb_decode_mx(const uint16_t* q_lat, const uint16_t* q_rope, const ui
                          int32_t max_len, int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
                          int32_t rope, float softmax_scale, float* out, int32_t num_splits,
                          void* workspace, size_t workspace_bytes, void* stream) {
-    // (the exponents take the place of the scales, with byte alignment)
+    // (the exponents take the place of the scales, 4-byte aligned)
     int rc = check_decode(q_lat, q_rope, codes, exps, kv_start, kv_len, max_len, B, Q, H, kv_lora,
-                          rope, softmax_scale, out, 1);
+                          rope, softmax_scale, out, 4);
     if (rc != KV8_OK) return rc;
     if (num_splits < 1 || num_splits > (1 << 20)) return KV8_EINVAL;
     kv8::DecodeLaunch d =
         make_launch(q_lat, q_rope, codes, nullptr, kv_start, kv_len, B, Q, H, softmax_scale, out);
+    d.exps = exps;
     d.n_sub = sub_splits(B, Q, H, num_splits);
     d.n_splits = num_splits * d.n_sub;
     if (d.n_splits > 1) {
-        const size_t need = kv8::mx_workspace_bytes(B, Q, H, d.n_splits);
+        const size_t need = kv8::splitT_workspace_bytes(B, Q, H, d.n_splits);
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KV8_EWORKSPACE;
         d.workspace = workspace;
     }
-    return launched(kv8::launch_absorb_decode_mx(d, exps, static_cast<hipStream_t>(stream)));
+    return launched(kv8::launch_absorb_decode(d, static_cast<hipStream_t>(stream)));
 }
 
 size_t kv8_mx_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora, int32_t num_splits) {
     if (B < 1 || Q < 1 || H < 1 || num_splits < 1 || kv_lora != kv8::kKvLora) return 0;
     const int total = num_splits * sub_splits(B, Q, H, num_splits);
-    return total > 1 ? kv8::mx_workspace_bytes(B, Q, H, total) : 0;
+    return total > 1 ? kv8::splitT_workspace_bytes(B, Q, H, total) : 0;
 }
 
 int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope, const uint8_t* codes,

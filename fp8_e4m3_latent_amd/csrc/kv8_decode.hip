@@ -88,7 +88,7 @@ struct DecodeArgs {
     const uint16_t* q_lat;
     const uint16_t* q_rope;
     const uint8_t* codes;
-    const float* scales;
+    const float* scales;   // per-row scales [rows][2] (or the exponents below)
     const int64_t* kv_start;
     const int32_t* kv_len;
     int B, Q, H, QH;
@@ -100,6 +100,7 @@ struct DecodeArgs {
     float* out;        // [B][QH][512] when no partials are written
     int16_t* part_o;   // [n_splits][B][QH][512] codes, O = code * o_scale
     float* part_ml;    // [n_splits][B][QH] RangeStat records (16 bytes each)
+    const uint8_t* exps;  // block exponents [rows][18] of block-scaled rows
 };
 
 // s_waitcnt with only the vector-memory counter limited (lgkm and exp free)
@@ -199,6 +200,38 @@ __device__ __forceinline__ uint4 dec8_f16(uint32_t w0, uint32_t w1) {
     return make_uint4(dec2_f16<false>(w0), dec2_f16<true>(w0), dec2_f16<false>(w1),
                       dec2_f16<true>(w1));
 }
+// the same times a power of two f <= 1 (block-scaled rows: 2^(E_block - E_max))
+__device__ __forceinline__ uint32_t dec2_f16s(uint32_t four_codes, float f, bool hi) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(four_codes, f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(four_codes, f, false));
+}
+__device__ __forceinline__ uint4 dec8_f16s(uint32_t w0, uint32_t w1, float f) {
+    return make_uint4(dec2_f16s(w0, f, false), dec2_f16s(w0, f, true), dec2_f16s(w1, f, false),
+                      dec2_f16s(w1, f, true));
+}
+// Block exponents of a block-scaled row: ue8m0 bytes, block b of the row at
+// byte 18 t + b of its tile's exponent copy (16 Lc blocks, then 2 Rc blocks).
+constexpr int kMxBlocksPerRow = (kKvLora + kRope) / 32;  // 18
+constexpr int kMxTileExpBytes = kTT * kMxBlocksPerRow;   // 576
+// largest of the 16 Lc exponent bytes of the row at byte a (even) of an LDS
+// exponent copy whose base is 4-byte aligned
+__device__ __forceinline__ int mx_lc_max(const uint8_t* base, int a) {
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(base + (a & ~3));
+    const uint32_t sh = 8 * (a & 3);      // 0 or 16
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t v = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);  // bytes 4 i .. 4 i + 3
+        m = max(m, max(max(v & 0xFFu, (v >> 8) & 0xFFu), max((v >> 16) & 0xFFu, v >> 24)));
+    }
+    return static_cast<int>(m);
+}
+// the 2 Rc exponent bytes of the row at byte a (even), low byte first
+__device__ __forceinline__ uint32_t mx_rc_pair(const uint8_t* base, int a) {
+    return *reinterpret_cast<const uint16_t*>(base + a + 16);
+}
+// 2^(E - 127) as a float (2^-127 for the byte 0 of an all-zero block)
+__device__ __forceinline__ float mx_pow2(int E) { return __builtin_ldexpf(1.0f, E - 127); }
 
 // Combine a per-lane value with the one in lane l ^ 32 (the other half of the
 // wave holds the other 16 tokens of the same query row).
@@ -342,12 +375,25 @@ __device__ __forceinline__ f16x8_t ctx_operand(const uint8_t* lc, int tb0, int t
 // the transpose reads (4 tokens x 64 bytes per 32 lanes), the decode reads
 // (tokens t and t + 4) and writes (tokens t and t + 4, both chunk parities).
 
+// kMX: block-scaled rows (e4m3 codes with one ue8m0 exponent per 32 values).
+// Each token's largest Lc and Rc block exponents E_L, E_R take the place of
+// the per-row scales (s = 2^(E - 127)), and its codes are decoded to fp16
+// times 2^(E_block - E_L) (or - E_R): exact for blocks within 2^15 of their
+// segment's largest, smaller blocks round to fp16 subnormals.  The tile's
+// exponent bytes (576) are copied where the per-row path copies its scale
+// pairs (256), and the Rc codes cycle through three buffers instead of four
+// to make room.
+template <bool kMX>
 __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p) {
+    constexpr int kRcB = kMX ? 3 : kRcBufs;                  // raw Rc buffers
+    // copied scales, or exponents (576 bytes from byte 0 or 2 of a 4-byte word)
+    constexpr int kScBytes = kMX ? kMxTileExpBytes + 16 : 8 * kTT;
     __shared__ __attribute__((aligned(16))) uint8_t s_raw[kNBuf][kRawLcBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_rc[kRcBufs][kRawRcBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_rc[kRcB][kRawRcBytes];
     __shared__ __attribute__((aligned(16))) uint8_t s_lc[kNBuf][kLcBytes];
-    __shared__ __attribute__((aligned(16))) float s_sc[kNBuf][2 * kTT];   // copied (Lc, Rc) scales
+    __shared__ __attribute__((aligned(16))) uint8_t s_scb[kNBuf][kScBytes];  // copied (Lc, Rc) scales or exponents
     __shared__ __attribute__((aligned(16))) float s_scd[kNBuf][3 * kTT];  // s_Lc, s_Rc, s_Lc / 2^e
+    auto rc_buf = [](int tile) { return kMX ? tile % kRcB : tile & (kRcBufs - 1); };
     __shared__ uint32_t s_red[3][kWaves];
     __shared__ int s_restart, s_shift;
     // per-row output factors of the epilogue, in the first raw Lc buffer (no
@@ -402,6 +448,15 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int64_t ntok = te > ts ? te - ts : 0;
     const int ntiles = static_cast<int>((ntok + kTT - 1) / kTT);
     const int64_t full_until = te < n_first ? te : n_first;  // no mask below this token
+    // (block-scaled rows: a tile's exponent bytes start at byte 0 or 2 of a
+    // 4-byte word, the same for every tile of the range)
+    const int mx_shift = kMX ? 2 * static_cast<int>((row_base + ts) & 1) : 0;
+    // rows of tile `tile` inside the range (the tiles past it re-copy the last)
+    auto tile_valid = [&](int tile) {
+        tile = tile < ntiles ? tile : ntiles - 1;
+        const int64_t left = te - (ts + static_cast<int64_t>(tile) * kTT);
+        return static_cast<int>(left < kTT ? left : kTT);
+    };
 
     // visible tokens of this lane's row in the range, relative to ts (rebuilt
     // where a tile needs masking, so that it is not kept live across the loop)
@@ -478,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // offsets do not depend on the tile; copy k's first row (8 k) goes into
     // the base.
     auto issue_copy = [&](int tile, int lbuf, int k, int ln) {
-        const int rbuf = tile & (kRcBufs - 1);  // (before the clamp)
+        const int rbuf = rc_buf(tile);  // (before the clamp)
         tile = tile < ntiles ? tile : ntiles - 1;
         const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
         const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
@@ -492,8 +547,19 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             copy_to_lds_b128_rc(base, static_cast<uint32_t>(valid * kRowBytes),
                                 static_cast<uint32_t>(dma_rc(ln)), lds_addr(&s_rc[rbuf][1024 * w]));
         } else if (w == 3) {
-            copy_to_lds_b32_rc(p.scales + 2 * (row_base + t0), static_cast<uint32_t>(8 * valid),
-                               static_cast<uint32_t>(4 * ln), lds_addr(&s_sc[lbuf][0]));
+            if constexpr (kMX) {
+                // the tile's 576 exponent bytes, 16 per lane on lanes 0-35; the
+                // range check counts whole dwords, so the last one may carry
+                // bytes of the row after the range (their tokens are masked
+                // and get zero scales in decode_scales)
+                if (ln < kScBytes / 16)
+                    copy_to_lds_b128_rc(p.exps + (row_base + t0) * kMxBlocksPerRow - mx_shift,
+                                        static_cast<uint32_t>((mx_shift + valid * kMxBlocksPerRow + 3) & ~3),
+                                        static_cast<uint32_t>(16 * ln), lds_addr(&s_scb[lbuf][0]));
+            } else {
+                copy_to_lds_b32_rc(p.scales + 2 * (row_base + t0), static_cast<uint32_t>(8 * valid),
+                                   static_cast<uint32_t>(4 * ln), lds_addr(&s_scb[lbuf][0]));
+            }
         }
     };
     // (outside the tile loop, with offsets rebuilt from a fresh lane id)
@@ -510,6 +576,33 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // ---- the range's largest Lc scale, largest Rc scale and smallest Lc
     //      scale (bit patterns of non-negative floats order as integers)
     uint32_t lbits = 0, rbits = 0, nbits = 0xFFFFFFFFu;
+    if constexpr (kMX) {
+        // a token's Lc and Rc scales are 2^(E - 127) for its largest block
+        // exponents E (the bytes of one row: 9 two-byte loads, all inside it)
+        const uint16_t* ex16 = reinterpret_cast<const uint16_t*>(p.exps);
+        for (int64_t t0 = ts + tid; t0 < te; t0 += 2 * kThreads) {  // two rows in flight
+            uint32_t v[2][9];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t t = t0 + u * kThreads;
+#pragma unroll
+                for (int i = 0; i < 9; ++i) v[u][i] = t < te ? ex16[(row_base + t) * 9 + i] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m = max(m, max(v[u][i] & 0xFFu, v[u][i] >> 8));
+                const uint32_t er = max(v[u][8] & 0xFFu, v[u][8] >> 8);
+                const uint32_t lb = __float_as_uint(mx_pow2(static_cast<int>(m)));
+                const uint32_t rb = __float_as_uint(mx_pow2(static_cast<int>(er)));
+                const bool in = t0 + u * kThreads < te;
+                lbits = in ? max(lbits, lb) : lbits;
+                rbits = in ? max(rbits, rb) : rbits;
+                nbits = in ? min(nbits, lb) : nbits;
+            }
+        }
+    } else
     for (int64_t t0 = ts + tid; t0 < te; t0 += 4 * kThreads) {  // four loads in flight
         uint2 v[4];
 #pragma unroll
@@ -655,17 +748,65 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         const uint8_t* raw = &s_raw[buf][0];
         draw[j & 1] = lds_load<uint4>(raw, ((j & 1) ? (d_rA ^ 128) : d_rA) + 256 * (j >> 1));
     };
+    // block-scaled rows: for the lane's four Lc blocks 4 j + s / 2 (s = lane
+    // % 8; the token's 8 lanes cover its 16 blocks) the exponent relative to
+    // the token's largest, E_block - E_L >= -128 as a signed byte j of
+    // mx_pack (below 2^-128 the fp16 value is 0 either way)
+    uint32_t mx_pack = 0;
+    auto mx_prep = [&](int buf) {
+        if constexpr (kMX) {
+            // (the lane's token and block rebuilt from a fresh lane id, so that
+            // no offset stays live across the tile loop)
+            const int ln = fresh_lane_id();
+            const int tok = 8 * w + (ln >> 4) + 4 * ((ln >> 3) & 1);
+            const uint8_t* ex = &s_scb[buf][mx_shift + kMxBlocksPerRow * tok + ((ln & 7) >> 1)];
+            int b[4];
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b[j] = ex[4 * j];
+                m = max(m, static_cast<uint32_t>(b[j]));
+            }
+            m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x4E, 0xF, 0xF, false)));
+            m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x141, 0xF, 0xF, false)));
+            mx_pack = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = b[j] - static_cast<int>(m);
+                mx_pack |= (static_cast<uint32_t>(d < -128 ? -128 : d) & 0xFFu) << (8 * j);
+            }
+        }
+    };
     auto decode_store = [&](int buf, int j, int half) {
         uint8_t* lc = &s_lc[buf][0];
         const uint4 r = draw[j & 1];
-        const uint4 v = half == 0 ? dec8_f16(r.x, r.y) : dec8_f16(r.z, r.w);
+        uint4 v;
+        if constexpr (kMX) {
+            const float f = __builtin_ldexpf(1.0f, static_cast<int>(mx_pack << (24 - 8 * j)) >> 24);
+            v = half == 0 ? dec8_f16s(r.x, r.y, f) : dec8_f16s(r.z, r.w, f);
+        } else {
+            v = half == 0 ? dec8_f16(r.x, r.y) : dec8_f16(r.z, r.w);
+        }
         *reinterpret_cast<uint4*>(lc + (half == 0 ? d_wA : (d_wA ^ 16)) + 256 * j) = v;
     };
     // (every wave writes the same values: lane t < 32 the signed s_Lc / 2^ex,
     // s_Rc / 2^ex of token t, lane 32 + t the value s_Lc / 2^e of token t,
     // twice)
-    auto decode_scales = [&](int buf) {
-        const float2 sc = *reinterpret_cast<const float2*>(&s_sc[buf][2 * l32]);
+    auto decode_scales = [&](int buf, int tile) {
+        float2 sc;
+        if constexpr (kMX) {
+            // 2^(E_L - 127), 2^(E_R - 127) of token l32; zero past the range
+            const uint8_t* base = &s_scb[buf][0];
+            const int tok = fresh_lane_id() & 31;
+            const int a = mx_shift + kMxBlocksPerRow * tok;
+            const uint32_t rp = mx_rc_pair(base, a);
+            const bool in = tok < tile_valid(tile);
+            sc.x = in ? mx_pow2(mx_lc_max(base, a)) : 0.0f;
+            sc.y = in ? mx_pow2(static_cast<int>(max(rp & 0xFFu, rp >> 8))) : 0.0f;
+        } else {
+            (void)tile;
+            sc = *reinterpret_cast<const float2*>(&s_scb[buf][8 * l32]);
+        }
         float* d = &s_scd[buf][0];
         const float v0 = __builtin_ldexpf(g == 0 ? sgn * sc.x : sc.x, g == 0 ? -ex : -e);
         const float v1 = g == 0 ? __builtin_ldexpf(sgn * sc.y, -ex) : v0;
@@ -715,16 +856,25 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     f16x8_t aq[kScoreAhead];
     uint4 rope[2];
     f16x8_t ropeop;
+    float mx_rf = 1.0f;  // block-scaled rows: 2^(E of Rc block g - E_R) of the lane's token
     auto rope_load = [&](int tile) {
-        const uint8_t* rc = &s_rc[tile & (kRcBufs - 1)][0];
+        const uint8_t* rc = &s_rc[rc_buf(tile)][0];
         const int ln = fresh_lane_id();
         const int rope_off = 16 * (ln + (ln & 32));  // (= 16 (64 g + l32))
         rope[0] = lds_load<uint4>(rc, rope_off);
         rope[1] = lds_load<uint4>(rc, rope_off + 16 * 32);
+        if constexpr (kMX) {
+            const uint32_t rp = mx_rc_pair(&s_scb[tile % kNBuf][0], mx_shift + kMxBlocksPerRow * (ln & 31));
+            const int eg = static_cast<int>((ln & 32) ? rp >> 8 : rp & 0xFFu);
+            mx_rf = __builtin_ldexpf(1.0f, eg - static_cast<int>(max(rp & 0xFFu, rp >> 8)));
+        }
     };
     auto rope_operand = [&](int r) {
         const uint4 c4 = rope[r >> 1];
-        ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
+        if constexpr (kMX)
+            ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16s(c4.z, c4.w, mx_rf) : dec8_f16s(c4.x, c4.y, mx_rf));
+        else
+            ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
     };
     auto score_begin = [&](int buf) {
         const uint8_t* lc = &s_lc[buf][0];
@@ -899,25 +1049,34 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // largest probability operand, which only a watched pass reads).
     auto run_pass = [&]() {
         if (ntiles > 0) {
+            mx_prep(0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 decode_load(0, j);
                 decode_store(0, j, 0);
                 decode_store(0, j, 1);
             }
-            decode_scales(0);
+            decode_scales(0, 0);
             end_barrier();  // tile 0 decoded; tile 1 landed, tile 2 may be in flight
-            issue_tile(3);  // (raw buffers of tile 0, decoded)
-            rope_load(0);
+            if constexpr (kMX) {
+                // (tile 3's Rc codes and exponents reuse tile 0's buffers)
+                rope_load(0);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue_tile(3);
+            } else {
+                issue_tile(3);  // (raw buffers of tile 0, decoded)
+                rope_load(0);
+            }
             score_begin(0);
             static_for<36>([&](auto kc) {
                 constexpr int ks = decltype(kc)::value;
                 score_step(0, ks);
                 // decode of tile 1 between the score MFMAs (as in phase A)
                 if constexpr (ks >= 6 && ks <= 30 && (ks - 6) % 8 == 0) decode_load(1, (ks - 6) / 8);
+                if constexpr (ks == 7) mx_prep(1);
                 if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(1, (ks - 9) / 8, 0);
                 if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(1, (ks - 11) / 8, 1);
-                if constexpr (ks == 35) decode_scales(1);
+                if constexpr (ks == 35) decode_scales(1, 1);
             });
             mfma_acc_drain(accL, accR);
             static_for<kSoftSteps>([&](auto k) { soft_step(decltype(k)::value, 0, 0, true); });
@@ -947,9 +1106,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 // decode of tile it + 2 between the score MFMAs (loads well
                 // ahead of their conversions and stores)
                 if constexpr (ks >= 6 && ks <= 30 && (ks - 6) % 8 == 0) decode_load(B2, (ks - 6) / 8);
+                if constexpr (ks == 7) mx_prep(B2);
                 if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(B2, (ks - 9) / 8, 0);
                 if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(B2, (ks - 11) / 8, 1);
-                if constexpr (ks == 35) decode_scales(B2);
+                if constexpr (ks == 35) decode_scales(B2, it + 2);
                 if constexpr (ks % 11 == 3) issue_copy(it + 4, B1, ks / 11, lane);
                 order();
             });
@@ -1316,445 +1476,6 @@ void launch_merge(const int16_t* part_o, const RangeStat* part_ml, int B, int QH
     }
 }
 
-// ---------------------------------------------------------------------------
-// Absorbed decode over block-scaled (MX) rows: e4m3 codes with one ue8m0
-// exponent per 32 values (page "Phase 0 toward V4.1 on a 128 GB Mac:
-// lossless mxfp8 residents and kill-test tooling", mxfp8 residents
-// paragraph; the decode itself follows "KV8=1: fp8 e4m3 latent KV cache
-// (CPU + CUDA) with .coli_kv v2" (colibri PR #299), commit message,
-// attention_rows item).
-//
-// Same blocks, token ranges and partials as absorb_decode_kernel, in a
-// simpler form: two passes over the range (row maxima, then weights and
-// context), one tile of 32 rows at a time (the next tile's copies in flight).
-// Each tile is decoded exactly into bf16: block b of token t as
-// dec(code) 2^(E_tb - E_t), with E_t the token's largest Lc (or Rc) block
-// exponent, so every value keeps its e4m3 bits; 2^(E_t - ex) multiplies the
-// token's score in f32 after the dot products (ex: the range's largest
-// exponent), and p 2^(E_t - eL) is the context's probability operand (eL: the
-// range's largest Lc exponent), split into two bf16 pieces (16 significant
-// bits) so that the context matches the fp16-operand precision of the
-// per-row path.  Queries are the bf16 values times 2^-kq (exact).
-// ---------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-constexpr int kMxBlocks = kRowBytes / 32;       // 18 exponent bytes per row
-constexpr int kMxVStride = 2 * kRowBytes + 16;  // 1168: bf16 row + padding
-constexpr int kMxExpBytes = 768;                // a tile's exponent bytes (+ alignment shift)
-
-struct DecodeMxArgs {
-    const uint16_t* q_lat;
-    const uint16_t* q_rope;
-    const uint8_t* codes;
-    const uint8_t* exps;
-    const int64_t* kv_start;
-    const int32_t* kv_len;
-    int B, Q, H, QH;
-    int n_rb, n_splits, n_sub;
-    float c;
-    float* out;
-    int16_t* part_o;
-    float* part_ml;
-};
-
-// (the "memory" clobbers keep the operand loads in their ring slots, so the
-// compiler does not pull loads of later steps above the MFMAs)
-__device__ __forceinline__ void mx_score_first(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b) : "memory");
-}
-__device__ __forceinline__ void mx_score(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b) : "memory");
-}
-// (its A operand comes from VALU packing: two wait states first)
-__device__ __forceinline__ void mx_ctx(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b) : "memory");
-}
-
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
-
-__global__ __launch_bounds__(kThreads, 1) void absorb_decode_mx_kernel(DecodeMxArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kTT * kRowBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_exp[2][kMxExpBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[kTT * kMxVStride];
-    __shared__ __attribute__((aligned(16))) float s_tok[3][kTT];  // score Lc, score Rc, context factors
-    __shared__ int s_tokE[2][kTT];                                 // E_t of the Lc and Rc blocks
-    __shared__ uint32_t s_red[2][kWaves];
-    __shared__ float s_row[kWaves][32];
-    // the waves' Rc query operands (bf16 times 2^-kq), rows of 144 bytes
-    __shared__ __attribute__((aligned(16))) uint8_t s_qr[kWaves][32 * 144];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 5;
-    const int l32 = lane & 31;
-
-    int bid = blockIdx.x;
-    if ((gridDim.x & 7) == 0) bid = (bid & 7) * static_cast<int>(gridDim.x >> 3) + (bid >> 3);
-    const int rb = bid % p.n_rb;
-    bid /= p.n_rb;
-    const int split = bid % p.n_splits;
-    const int b = bid / p.n_splits;
-    const int row0 = rb * kRowsPerBlock;
-    const int row = row0 + 32 * w + l32;
-    const bool row_ok = row < p.QH;
-
-    const int64_t L = load_uniform(p.kv_len + b);
-    const int64_t row_base = load_uniform(p.kv_start + b);
-    const int n_outer = p.n_splits / p.n_sub;
-    const int outer = split / p.n_sub, sub = split % p.n_sub;
-    const int64_t chunk = (L + n_outer - 1) / n_outer;
-    const int64_t sub_chunk = (chunk + p.n_sub - 1) / p.n_sub;
-    const int64_t o0 = static_cast<int64_t>(outer) * chunk;
-    int64_t ts = o0 + static_cast<int64_t>(sub) * sub_chunk;
-    int64_t te = ts + sub_chunk < o0 + chunk ? ts + sub_chunk : o0 + chunk;
-    te = L < te ? L : te;
-    const int row_hi = (p.QH < row0 + kRowsPerBlock ? p.QH : row0 + kRowsPerBlock) - 1;
-    const int64_t n_first = L - (p.Q - 1) + row0 / p.H;
-    const int64_t n_last = L - (p.Q - 1) + row_hi / p.H;
-    te = te < n_last ? te : n_last;
-    const int64_t ntok = te > ts ? te - ts : 0;
-    const int ntiles = static_cast<int>((ntok + kTT - 1) / kTT);
-    const int64_t full_until = te < n_first ? te : n_first;
-    if (ntiles == 0 && p.part_o != nullptr) {
-        if (g == 0 && row_ok) {
-            float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 4;
-            *reinterpret_cast<float4*>(ml) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        }
-        return;
-    }
-    const int64_t n_row = row_ok ? L - (p.Q - 1) + row / p.H : 0;
-    const int lim_rel0 = static_cast<int>((n_row < te ? n_row : te) - ts);
-
-    // ---- the range's largest Lc block exponent and largest exponent overall
-    uint32_t eLb = 0, eAb = 0;
-    {
-        const uint8_t* e0 = p.exps + (row_base + ts) * kMxBlocks;
-        const int64_t nb = ntok * kMxBlocks;
-        for (int64_t k = tid; k < nb; k += kThreads) {
-            const uint32_t v = e0[k];
-            eAb = max(eAb, v);
-            eLb = (k % kMxBlocks) < 16 ? max(eLb, v) : eLb;
-        }
-    }
-    eLb = wave_max_u32(eLb);
-    eAb = wave_max_u32(eAb);
-    if (lane == 0) {
-        s_red[0][w] = eLb;
-        s_red[1][w] = eAb;
-    }
-
-    // ---- query row of this lane (bf16 B operands times 2^-kq): Lc k-step ks
-    //      holds columns 16 ks + 8 g .. +8, Rc k-step r columns 16 r + 8 g ..
-    uint4 qv[36];
-    {
-        const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
-        const uint4* ql = reinterpret_cast<const uint4*>(p.q_lat + qrow * kKvLora);
-        const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) qv[ks] = ql[2 * ks + g];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) qv[32 + r] = qr[2 * r + g];
-    }
-    int kq = 0;
-    {
-        uint32_t m2 = 0;
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks)
-            m2 = absmax2_bf16x2(absmax2_bf16x2(absmax2_bf16x2(absmax2_bf16x2(m2, qv[ks].x), qv[ks].y),
-                                               qv[ks].z), qv[ks].w);
-        const uint32_t mbits = max(m2 << 16, m2 & 0xFFFF0000u);
-        const float qmax = fmaxf(__uint_as_float(mbits), other_half(__uint_as_float(mbits)));
-        if (qmax > 0.0f) {
-            kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 12;
-            kq = kq < -100 ? -100 : (kq > 120 ? 120 : kq);
-        }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-        uint4 v = qv[ks];
-        auto sc = [&](uint32_t w2) {
-            const uint32_t lo = __float_as_uint(__builtin_ldexpf(bf16_lo(w2), -kq)) >> 16;
-            const uint32_t hi = __float_as_uint(__builtin_ldexpf(bf16_hi(w2), -kq)) & 0xFFFF0000u;
-            return lo | hi;
-        };
-        qv[ks] = make_uint4(sc(v.x), sc(v.y), sc(v.z), sc(v.w));
-    }
-    // (the Rc operands wait in LDS: fewer registers live through the tile loop)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<uint4*>(&s_qr[w][144 * l32 + 32 * r + 16 * g]) = qv[32 + r];
-    __syncthreads();
-    eLb = max(max(s_red[0][0], s_red[0][1]), max(s_red[0][2], s_red[0][3]));
-    eAb = max(max(s_red[1][0], s_red[1][1]), max(s_red[1][2], s_red[1][3]));
-    const int eL = __builtin_amdgcn_readfirstlane(static_cast<int>(eLb) - 127);
-    const int ex = __builtin_amdgcn_readfirstlane(static_cast<int>(eAb) - 127);
-
-    const float sgn = p.c >= 0.0f ? 1.0f : -1.0f;
-    float c_row = __builtin_ldexpf(fabsf(p.c), kq + ex);
-    if (!(c_row <= FLT_MAX)) c_row = FLT_MAX;
-    if (c_row < FLT_MIN) c_row = FLT_MIN;
-
-    // ---- tile copies: codes as 18 copies of 1 KiB (wave w takes w, w + 4, ..),
-    //      exponents as three 256-byte copies from the dword at or below the
-    //      tile's first byte (range-checked: rows past the range read zeros)
-    auto issue_tile = [&](int tile, int buf) {
-        const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
-        const int valid = static_cast<int>(te - t0 < kTT ? te - t0 : kTT);
-        const int ln = fresh_lane_id();
-        const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
-#pragma unroll
-        for (int k = 0; k < 5; ++k) {
-            const int i = w + kWaves * k;
-            if (i < kMxBlocks)
-                copy_to_lds_b128_rc(base, static_cast<uint32_t>(valid * kRowBytes),
-                                    static_cast<uint32_t>(1024 * i + 16 * ln), lds_addr(&s_raw[buf][1024 * i]));
-        }
-        if (w < 3) {
-            // (the range check zeroes a dword that ends past num_records, so the
-            // count is rounded up to whole dwords; the bytes it lets in belong to
-            // rows past the range, whose exponents are never used)
-            const int64_t a = (row_base + t0) * kMxBlocks;
-            const int64_t a4 = a & ~int64_t(3);
-            copy_to_lds_b32_rc(p.exps + a4, static_cast<uint32_t>((a - a4 + valid * kMxBlocks + 3) & ~3),
-                               static_cast<uint32_t>(256 * w + 4 * ln), lds_addr(&s_exp[buf][256 * w]));
-        }
-    };
-    const int exp_shift = static_cast<int>(((row_base + ts) * kMxBlocks) & 3);  // (t0 - ts is a multiple of 32)
-
-    // per-lane LDS offsets: score A operand (token l32, columns 16 ks + 8 g)
-    const int sc_off = l32 * kMxVStride + 16 * g;
-    // context B operand: transposed reads, lane (G, gi) of k-group g takes
-    // token 4 g + 8 h + gi / 4 (+ 16 kc), columns 32 dt + 16 (G % 2) + 4 (gi % 4)
-    const int G = lane >> 4, gi = lane & 15;
-    const int tb0 = (4 * g + (gi >> 2)) * kMxVStride + 2 * (16 * (G & 1) + 4 * (gi & 3));
-    const int tb1 = tb0 + 8 * kMxVStride;
-
-    // the context of 256 columns at a time: half h in pass 1 + h
-    f32x16_t O[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) zero_acc(O[dt]);
-    float m_x = -INFINITY;  // row maximum of x (pass 0)
-    float l_run = 0.0f;     // this lane's half of the row sum (pass 1)
-
-    // out = 2^eL (O / l) for columns 256 h ..: to the output, or (split
-    // partials) to the f32 rows of the range's normalised context
-    auto write_half = [&](int h) {
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                     : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]), "+a"(O[6]),
-                       "+a"(O[7]));
-        const float l_tot = pair_sum(l_run);
-        const int el = fresh_lane_id();
-        const int e32 = el & 31, eg = el >> 5;
-        if (eg == 0) s_row[w][e32] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        __builtin_amdgcn_wave_barrier();
-        float* dst = p.part_o == nullptr
-                         ? p.out + static_cast<int64_t>(b) * p.QH * kKvLora
-                         : reinterpret_cast<float*>(p.part_o) + (static_cast<int64_t>(split) * p.B + b) * p.QH * kKvLora;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 f4 = *reinterpret_cast<const float4*>(&s_row[w][8 * q4 + 4 * eg]);
-            const float fv[4] = {f4.x, f4.y, f4.z, f4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int orow = row0 + 32 * w + 8 * q4 + 4 * eg + r;
-                if (orow < p.QH) {
-                    float* o = dst + static_cast<int64_t>(orow) * kKvLora + 256 * h + e32;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) {
-                        float v;
-                        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(O[dt][4 * q4 + r]));
-                        o[32 * dt] = __builtin_ldexpf(v * fv[r], eL);
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-    };
-
-    for (int pass = 0; pass < 3; ++pass) {
-        const int half = pass - 1;
-        issue_tile(0, 0);
-        const float ref = m_x == -INFINITY ? 0.0f : m_x;
-        float mx_lane = -INFINITY;
-        for (int it = 0; it < ntiles; ++it) {
-            const int buf = it & 1;
-            wait_all_copies();
-            __syncthreads();  // tile it landed in every wave; the last tile's reads are done
-            if (it + 1 < ntiles) issue_tile(it + 1, buf ^ 1);
-            if (tid < kTT) {  // token statistics (rows past the range: zero factors)
-                const int64_t t0 = ts + static_cast<int64_t>(it) * kTT;
-                const bool in = t0 + tid < te;
-                const uint8_t* e = &s_exp[buf][exp_shift + kMxBlocks * tid];
-                int EL = 0, ER = max(static_cast<int>(e[16]), static_cast<int>(e[17]));
-#pragma unroll
-                for (int k = 0; k < 16; ++k) EL = max(EL, static_cast<int>(e[k]));
-                EL -= 127;
-                ER -= 127;
-                s_tok[0][tid] = in ? __builtin_ldexpf(sgn, EL - ex) : 0.0f;
-                s_tok[1][tid] = in ? __builtin_ldexpf(sgn, ER - ex) : 0.0f;
-                s_tok[2][tid] = in ? __builtin_ldexpf(1.0f, EL - eL) : 0.0f;
-                s_tokE[0][tid] = in ? EL : 1000;  // (decodes the row's blocks with factor 0)
-                s_tokE[1][tid] = in ? ER : 1000;
-            }
-            __syncthreads();
-            // decode: thread k converts the Lc block pair k % 8 of token k / 8, and
-            // the first 32 threads the Rc block pair of token k (64 codes each)
-            auto decode_pair = [&](int t, int bp, int Eref) {
-                const uint8_t* e = &s_exp[buf][exp_shift + kMxBlocks * t + 2 * bp];
-                const int d0 = static_cast<int>(e[0]) - 127 - Eref, d1 = static_cast<int>(e[1]) - 127 - Eref;
-                // (d <= 0 for the row's own blocks; a block more than 2^126 below
-                // the row's largest, or a row past the range, gets factor 0)
-                const float f0 = d0 < -126 || d0 > 0 ? 0.0f : __builtin_ldexpf(1.0f, d0);
-                const float f1 = d1 < -126 || d1 > 0 ? 0.0f : __builtin_ldexpf(1.0f, d1);
-                const uint8_t* src = &s_raw[buf][kRowBytes * t + 64 * bp];
-                uint8_t* dst = &s_v[kMxVStride * t + 128 * bp];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 r = *reinterpret_cast<const uint4*>(src + 16 * j);
-                    const float f = j < 2 ? f0 : f1;
-                    const uint32_t wv[4] = {r.x, r.y, r.z, r.w};
-                    uint32_t o[8];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[q], f, false));
-                        o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[q], f, true));
-                    }
-                    *reinterpret_cast<uint4*>(dst + 32 * j) = make_uint4(o[0], o[1], o[2], o[3]);
-                    *reinterpret_cast<uint4*>(dst + 32 * j + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-                }
-            };
-            {
-                const int k = fresh_lane_id() + 64 * w;
-                decode_pair(k >> 3, k & 7, s_tokE[0][k >> 3]);
-                if (w == 0 && k < kTT) decode_pair(k, 8, s_tokE[1][k]);
-            }
-            __syncthreads();
-
-            // (k-step k < 4: Rc columns 16 k; k >= 4: Lc columns 16 (k - 4); operands
-            // three steps ahead, placed by scheduling barriers)
-            f32x16_t accL, accR;
-            {
-                auto a_off = [&](int k) { return sc_off + (k < 4 ? 2 * (kKvLora + 16 * k) : 32 * (k - 4)); };
-                bf16x8_t a[3];
-#pragma unroll
-                for (int k = 0; k < 3; ++k) a[k] = *reinterpret_cast<const bf16x8_t*>(&s_v[a_off(k)]);
-                order();
-                static_for<36>([&](auto kc) {
-                    constexpr int k = decltype(kc)::value;
-                    const bf16x8_t av = a[k % 3];
-                    if constexpr (k + 3 < 36) a[k % 3] = *reinterpret_cast<const bf16x8_t*>(&s_v[a_off(k + 3)]);
-                    bf16x8_t qb;
-                    if constexpr (k < 4)
-                        qb = *reinterpret_cast<const bf16x8_t*>(&s_qr[w][144 * l32 + 32 * k + 16 * g]);
-                    else
-                        qb = __builtin_bit_cast(bf16x8_t, qv[k - 4]);
-                    if constexpr (k == 0) mx_score_first(accR, av, qb);
-                    else if constexpr (k < 4) mx_score(accR, av, qb);
-                    else if constexpr (k == 4) mx_score_first(accL, av, qb);
-                    else mx_score(accL, av, qb);
-                    order();
-                });
-            }
-            mfma_acc_drain(accL, accR);
-            // x for tokens 8 (j / 4) + 4 g + j % 4 of the tile, masked past the row's limit
-            float x[16];
-            const int rel = lim_rel0 - it * kTT - 4 * g;
-            const bool maskable = ts + static_cast<int64_t>(it) * kTT + kTT > full_until;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 sl = *reinterpret_cast<const float4*>(&s_tok[0][8 * q4 + 4 * g]);
-                const float4 sr = *reinterpret_cast<const float4*>(&s_tok[1][8 * q4 + 4 * g]);
-                const float slv[4] = {sl.x, sl.y, sl.z, sl.w}, srv[4] = {sr.x, sr.y, sr.z, sr.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 4 * q4 + r;
-                    x[j] = __builtin_fmaf(slv[r], accL[j], srv[r] * accR[j]);
-                    if (maskable && 8 * q4 + r >= rel) x[j] = -INFINITY;
-                }
-            }
-            if (pass == 0) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) mx_lane = fmaxf(mx_lane, x[j]);
-                continue;
-            }
-            // weights and their sum; the probability operands p 2^(E_t - eL)
-            float lsum = 0.0f;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 se = *reinterpret_cast<const float4*>(&s_tok[2][8 * q4 + 4 * g]);
-                const float sev[4] = {se.x, se.y, se.z, se.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 4 * q4 + r;
-                    const float pj = __builtin_amdgcn_exp2f(c_row * (x[j] - ref));
-                    lsum += pj;
-                    x[j] = pj * sev[r];
-                }
-            }
-            if (half == 0) l_run += lsum;
-            // context: O[dt] += (hi + lo) (32 rows x 16 tokens) . V (16 tokens x 32
-            // columns), the operands split in two bf16 pieces per 16-token chunk
-            auto ctx_b = [&](int n) {
-                const int off = (n >> 4) * 16 * kMxVStride + 64 * (n & 15);
-                const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t*)(&s_v[tb0 + off]));
-                const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t*)(&s_v[tb1 + off]));
-                const uint2 a2 = __builtin_bit_cast(uint2, v0), b2 = __builtin_bit_cast(uint2, v1);
-                return __builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, b2.x, b2.y));
-            };
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                uint32_t h[4], l[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float v0 = x[8 * kc + 2 * q], v1 = x[8 * kc + 2 * q + 1];
-                    const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
-                    h[q] = h0 | (h1 << 16);
-                    l[q] = bf16_bits_rne(v0 - bf16_value(h0)) | (bf16_bits_rne(v1 - bf16_value(h1)) << 16);
-                }
-                const bf16x8_t hv = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-                const bf16x8_t lv = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
-                bf16x8_t bq[2];
-                bq[0] = ctx_b(16 * kc + 8 * half);
-                bq[1] = ctx_b(16 * kc + 8 * half + 1);
-                order();
-                static_for<8>([&](auto nc) {
-                    constexpr int dt = decltype(nc)::value;
-                    const bf16x8_t bv = bq[dt % 2];
-                    if constexpr (dt + 2 < 8) bq[dt % 2] = ctx_b(16 * kc + 8 * half + dt + 2);
-                    mx_ctx(O[dt], hv, bv);
-                    mx_ctx(O[dt], lv, bv);
-                    order();
-                });
-            }
-        }
-        if (pass == 0) m_x = pair_max(mx_lane);
-        wait_all_copies();
-        __syncthreads();
-        if (pass > 0) {
-            write_half(half);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) zero_acc(O[dt]);
-        }
-    }
-
-    // ---------------- statistics of the split partials
-    const float l_tot = pair_sum(l_run);
-    if (p.part_o != nullptr && (fresh_lane_id() >> 5) == 0 && row_ok) {
-        float* ml = p.part_ml + ((static_cast<int64_t>(split) * p.B + b) * p.QH + row) * 4;
-        const double m_true = __builtin_ldexp(static_cast<double>(sgn * m_x), kq + ex);
-        const uint64_t mb = __builtin_bit_cast(uint64_t, m_true);
-        *reinterpret_cast<float4*>(ml) = make_float4(__uint_as_float(static_cast<uint32_t>(mb)),
-                                                     __uint_as_float(static_cast<uint32_t>(mb >> 32)), l_tot, 1.0f);
-    }
-}
-
 }  // namespace
 
 size_t splitT_workspace_bytes(int B, int Q, int H, int n_splits) {
@@ -1768,6 +1489,7 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) 
     a.q_rope = d.q_rope;
     a.codes = d.codes;
     a.scales = d.scales;
+    a.exps = d.exps;
     a.kv_start = d.kv_start;
     a.kv_len = d.kv_len;
     a.B = d.B;
@@ -1788,102 +1510,16 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) 
         a.part_ml = reinterpret_cast<float*>(a.part_o + rows * kKvLora);
     }
     const int64_t blocks = static_cast<int64_t>(d.B) * a.n_splits * a.n_rb;
-    hipLaunchKernelGGL(absorb_decode_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
-                       0, stream, a);
+    if (d.exps != nullptr)
+        hipLaunchKernelGGL(absorb_decode_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL(absorb_decode_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
+                           0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;
     if (d.n_splits > 1 && merge) {
         launch_merge(a.part_o, reinterpret_cast<const RangeStat*>(a.part_ml), d.B, a.QH, d.n_splits, a.c,
                      d.out, stream);
-        if (hipGetLastError() != hipSuccess) return -1;
-    }
-    return 0;
-}
-
-namespace {
-
-// Log-sum-exp merge of f32 partials (the block-scaled decode's): one wave per
-// (b, row), lane k summing columns 8 k .. 8 k + 7 over the ranges; the
-// weights w_s l_s / L are formed from the statistics first, as in
-// lse_merge_rows_kernel.
-__global__ __launch_bounds__(256) void lse_merge_f32_kernel(const float* __restrict__ part_v,
-                                                            const RangeStat* __restrict__ st, int B, int QH,
-                                                            int n_splits, float c, float* __restrict__ out) {
-    const int lane = threadIdx.x & 63;
-    const int64_t br = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int64_t stride = static_cast<int64_t>(B) * QH;
-    if (br >= stride) return;
-    const bool cpos = c >= 0.0f;
-    const double cabs = fabs(static_cast<double>(c));
-    double kmax = -INFINITY;
-    for (int s = lane; s < n_splits; s += 64) kmax = fmax(kmax, range_key(st[s * stride + br], cpos));
-    kmax = wave_max_f64(kmax);
-    float lsum = 0.0f;
-    if (kmax > -INFINITY)
-        for (int s = lane; s < n_splits; s += 64) {
-            const RangeStat r = st[s * stride + br];
-            lsum += range_weight(r, cpos, cabs, kmax) * r.l;
-        }
-    lsum = wave_sum_f32(lsum);
-    float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-    if (lsum > 0.0f) {
-        const float inv = 1.0f / lsum;
-        for (int s = 0; s < n_splits; ++s) {
-            const RangeStat r = st[s * stride + br];
-            const float wgt = range_weight(r, cpos, cabs, kmax) * r.l * inv;
-            if (wgt == 0.0f) continue;  // (uniform: skips empty ranges, whose rows are not written)
-            const float* v = part_v + (s * stride + br) * kKvLora + 8 * lane;
-            const float4 v0 = *reinterpret_cast<const float4*>(v), v1 = *reinterpret_cast<const float4*>(v + 4);
-            a0.x += wgt * v0.x; a0.y += wgt * v0.y; a0.z += wgt * v0.z; a0.w += wgt * v0.w;
-            a1.x += wgt * v1.x; a1.y += wgt * v1.y; a1.z += wgt * v1.z; a1.w += wgt * v1.w;
-        }
-    }
-    float* o = out + br * kKvLora + 8 * lane;
-    *reinterpret_cast<float4*>(o) = a0;
-    *reinterpret_cast<float4*>(o + 4) = a1;
-}
-
-}  // namespace
-
-size_t mx_workspace_bytes(int B, int Q, int H, int n_splits) {
-    const size_t rows = static_cast<size_t>(n_splits) * B * Q * H;
-    return rows * kKvLora * sizeof(float) + rows * sizeof(RangeStat);
-}
-
-int launch_absorb_decode_mx(const DecodeLaunch& d, const uint8_t* exps, hipStream_t stream) {
-    DecodeMxArgs a;
-    a.q_lat = d.q_lat;
-    a.q_rope = d.q_rope;
-    a.codes = d.codes;
-    a.exps = exps;
-    a.kv_start = d.kv_start;
-    a.kv_len = d.kv_len;
-    a.B = d.B;
-    a.Q = d.Q;
-    a.H = d.H;
-    a.QH = d.Q * d.H;
-    a.n_rb = (a.QH + kRowsPerBlock - 1) / kRowsPerBlock;
-    a.n_splits = d.n_splits;
-    a.n_sub = d.n_sub > 0 ? d.n_sub : 1;
-    a.c = d.softmax_scale * 1.4426950408889634f;
-    a.out = d.out;
-    a.part_o = nullptr;
-    a.part_ml = nullptr;
-    // f32 partials: rows of the normalised context, then the statistics
-    float* part_v = nullptr;
-    if (d.n_splits > 1) {
-        const size_t rows = static_cast<size_t>(d.n_splits) * d.B * a.QH;
-        part_v = static_cast<float*>(d.workspace);
-        a.part_o = reinterpret_cast<int16_t*>(part_v);
-        a.part_ml = part_v + rows * kKvLora;
-    }
-    const int64_t blocks = static_cast<int64_t>(d.B) * a.n_splits * a.n_rb;
-    hipLaunchKernelGGL(absorb_decode_mx_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0,
-                       stream, a);
-    if (hipGetLastError() != hipSuccess) return -1;
-    if (d.n_splits > 1) {
-        const int64_t rows = static_cast<int64_t>(d.B) * a.QH;
-        hipLaunchKernelGGL(lse_merge_f32_kernel, dim3(static_cast<uint32_t>((rows + 3) / 4)), dim3(256), 0, stream,
-                           part_v, reinterpret_cast<const RangeStat*>(a.part_ml), d.B, a.QH, d.n_splits, a.c, d.out);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;

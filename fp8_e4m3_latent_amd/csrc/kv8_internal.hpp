@@ -36,7 +36,8 @@ struct DecodeLaunch {
     const uint16_t* q_lat;
     const uint16_t* q_rope;
     const uint8_t* codes;
-    const float* scales;
+    const float* scales;            // per-row scales, or
+    const uint8_t* exps = nullptr;  // block exponents of block-scaled rows
     const int64_t* kv_start;
     const int32_t* kv_len;
     int B, Q, H;
@@ -51,11 +52,6 @@ struct DecodeLaunch {
 size_t splitT_workspace_bytes(int B, int Q, int H, int n_splits);
 // decode kernel (+ merge when n_splits > 1 and `merge` is set)
 int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge = true);
-// the same decode over block-scaled rows (codes + ue8m0 exponents [rows][18]);
-// equal ranges cut into n_sub sub-ranges, n_splits > 1 needs the workspace
-int launch_absorb_decode_mx(const DecodeLaunch& d, const uint8_t* exps, hipStream_t stream);
-// its workspace: f32 partials [n_splits][B][Q*H][512], then 16-byte statistics
-size_t mx_workspace_bytes(int B, int Q, int H, int n_splits);
 int launch_lse_merge(const void* partials, int B, int QH, int n_splits, float softmax_scale,
                      float* out, hipStream_t stream);
 

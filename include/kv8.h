@@ -236,17 +236,18 @@ int kv8_absorb_decode_splitT(const uint16_t* q_lat, const uint16_t* q_rope,
 
 /* Absorbed decode over block-scaled (MX) rows (codes and exponents from
  * kv8_quantize_rows_mx): the same arguments, ranges, workspace and result as
- * kv8_absorb_decode_splitT (workspace: kv8_mx_workspace_bytes, which holds
- * f32 partials), with exps (uint8 [*][(kv_lora + rope) / 32],
- * block b of row r scaled by 2^(exps[r][b] - 127)) in place of the scales:
- * s_t = softmax_scale * (q_lat . xhat_Lc[t] + q_rope . xhat_Rc[t]), out =
- * sum_t softmax(s)_t xhat_Lc[t], xhat = decode(code) * 2^(exp - 127).  The
- * products are exact (each row's Lc and Rc segments are decoded exactly to
- * bf16 relative to the segment's largest block; bf16 queries), and the
- * probabilities enter the context as two bf16 pieces (16 significant bits).
- * Blocks more than 2^126 below the largest block of their segment are read
- * as zero.  The kernel reads each token range three times (row maxima, then
- * the context in two halves of 256 columns). */
+ * kv8_absorb_decode_splitT, with exps (uint8 [*][(kv_lora + rope) / 32],
+ * 4-byte aligned, block b of row r scaled by 2^(exps[r][b] - 127)) in place
+ * of the scales: s_t = softmax_scale * (q_lat . xhat_Lc[t] + q_rope .
+ * xhat_Rc[t]), out = sum_t softmax(s)_t xhat_Lc[t], xhat = decode(code) *
+ * 2^(exp - 127).  The kernel of kv8_absorb_decode runs it: each row's largest
+ * Lc and Rc block exponents act as its two scales, and its codes enter the
+ * fp16 operands times 2^(E_block - E_largest), exact for blocks within 2^15
+ * of their segment's largest (smaller blocks round to fp16 subnormals, an
+ * error below 2^-15 of that segment's largest values); everything else,
+ * accuracy included, is as for the per-row scales.  The copies read the
+ * exponent array's last 4-byte word whole.  workspace: kv8_mx_workspace_bytes
+ * (the same partials as kv8_absorb_decode_splitT). */
 size_t kv8_mx_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t kv_lora,
                               int32_t num_splits);
 int kv8_absorb_decode_mx(const uint16_t* q_lat, const uint16_t* q_rope,

@@ -595,7 +595,7 @@ def main():
                     help="query rows the oracle times for the CPU baseline (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

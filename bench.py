@@ -514,6 +514,20 @@ def leg_project(torch, kv8, steps):
         else:
             res["f32_out"] = rec
         del out
+    # context: the library bf16 GEMM (torch.matmul) of the same shape on bf16
+    # operands, without the fp8 decode, row scale or Rc output
+    a16 = torch.randn((n, KL), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((n, N), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: torch.matmul(a16, w.t(), out=out)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    st = timer_stats(torch, steps, fn)
+    res["library_bf16_gemm"] = {
+        **st, "tflops": flops / (st["ms"] * 1e-3) / 1e12,
+        "what": "torch.matmul bf16 [8192, 512] x [512, 32768] -> bf16 (same shape, bf16 operands, "
+                "no decode): the vendor GEMM as a reference for this K=512 shape"}
+    del a16, out
     del codes, scales, w, rope
     torch.cuda.empty_cache()
     return res

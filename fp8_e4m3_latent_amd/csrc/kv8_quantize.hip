@@ -147,6 +147,24 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     const int64_t row0 =
         (static_cast<int64_t>(blockIdx.x) * kQuantWaves + (threadIdx.x >> 6)) * kRowsPerWave;
     if (row0 >= n_rows) return;
+    // producer: the positions are loaded before the rows, so that the
+    // rotation factors (which need only them) are computed while the row
+    // loads are in flight (vector loads complete in order)
+    float rpos = 0.0f;
+    float fq[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // this lane's frequencies (lane-indexed)
+    if constexpr (kProducer) {
+        const int64_t rrow = kRowsPerWave == 8 ? row0 + (lane >> 3) : row0;
+        rpos = static_cast<float>(pa.positions[rrow < n_rows ? rrow : row0]);
+        if constexpr (kRowsPerWave == 8) {  // pairs 4 (lane % 8) .. +3
+#pragma unroll
+            for (int t = 0; t < 4; ++t) fq[t] = pa.freq[4 * (lane & 7) + t];
+        } else {  // pairs 2 (lane % 16), +1
+            fq[0] = pa.freq[2 * (lane & 15)];
+            fq[1] = pa.freq[2 * (lane & 15) + 1];
+        }
+        // keep these loads ahead of the row loads
+        asm volatile("" ::: "memory");
+    }
     float4 a[kRowsPerWave], b[kRowsPerWave], c[kRowsPerWave];
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
@@ -155,16 +173,19 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
         const float* x = src + row * stride;
         a[r] = load_stream(x + 4 * lane);
         b[r] = load_stream(x + 256 + 4 * lane);
-        c[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (lane < 16) c[r] = load_stream(x + kKvLora + 4 * lane);
+        // Rc: every lane loads (lanes 16-63 repeat the 256 bytes of lanes
+        // 0-15, the same lines) and lanes 16-63 then hold zeros.  A load
+        // under a lane branch would end in a wait for every load in flight.
+        const float4 rc = load_stream(x + kKvLora + 4 * (lane & 15));
+        c[r] = lane < 16 ? rc : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    // producer: nothing that waits for the position moves between the row loads
+    if constexpr (kProducer) __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (kProducer) {
-        // Lc weights of the lane's columns; frequencies of pairs 2 l, 2 l + 1
+        // Lc weights of the lane's columns
         const float4 wa = *reinterpret_cast<const float4*>(pa.norm_weight + 4 * lane);
         const float4 wb = *reinterpret_cast<const float4*>(pa.norm_weight + 256 + 4 * lane);
-        const float f0 = pa.freq[2 * (lane & 15)];
-        const float f1 = pa.freq[2 * (lane & 15) + 1];
         // With eight rows, the 8 x 32 rotations of the wave are spread over all
         // lanes: lane L computes (cos, sin) of pairs 4 (L % 8) .. +3 of row L / 8
         // into this wave's LDS area, [row][pair][cos, sin], where lane l < 16
@@ -173,18 +194,23 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
         if constexpr (kRowsPerWave == 8) {
             __shared__ __attribute__((aligned(16))) float s_rot[kQuantWaves][8 * 32 * 2];
             rot = &s_rot[threadIdx.x >> 6][0];
-            const int64_t rrow = row0 + (lane >> 3) < n_rows ? row0 + (lane >> 3) : row0;
-            const float rpos = static_cast<float>(pa.positions[rrow]);
             float cv[4], sv[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                sincosf(reduce_angle(rpos * pa.freq[4 * (lane & 7) + t]), &sv[t], &cv[t]);
+                sincosf(reduce_angle(rpos * fq[t]), &sv[t], &cv[t]);
             *reinterpret_cast<float4*>(rot + 8 * lane) = make_float4(cv[0], sv[0], cv[1], sv[1]);
             *reinterpret_cast<float4*>(rot + 8 * lane + 4) = make_float4(cv[2], sv[2], cv[3], sv[3]);
         }
+        // one row per wave: the row's own two pairs, before its loads are waited for
+        float s0r = 0.0f, c0r = 0.0f, s1r = 0.0f, c1r = 0.0f;
+        if constexpr (kRowsPerWave == 1) {
+            if (lane < 16) {
+                sincosf(reduce_angle(rpos * fq[0]), &s0r, &c0r);
+                sincosf(reduce_angle(rpos * fq[1]), &s1r, &c1r);
+            }
+        }
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
-            const int64_t row = row0 + r < n_rows ? row0 + r : row0;
             float4& u = a[r];
             float4& v = b[r];
             float ss = u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
@@ -199,9 +225,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
                     const float4 t = *reinterpret_cast<const float4*>(rot + 64 * r + 4 * lane);
                     c0 = t.x; s0 = t.y; c1 = t.z; s1 = t.w;
                 } else {
-                    const float pos = static_cast<float>(pa.positions[row]);
-                    sincosf(reduce_angle(pos * f0), &s0, &c0);
-                    sincosf(reduce_angle(pos * f1), &s1, &c1);
+                    c0 = c0r; s0 = s0r; c1 = c1r; s1 = s1r;
                 }
                 const float4 q = c[r];
                 c[r] = make_float4(q.x * c0 - q.y * s0, q.x * s0 + q.y * c0,

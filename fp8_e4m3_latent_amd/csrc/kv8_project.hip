@@ -21,7 +21,7 @@
 // +128 by columns 64 (w % 4) .. +64 with eight 32x32 accumulators (bf16 MFMA
 // 32x32x16, f32 accumulation): 768 LDS bytes per MFMA.  Two waves share each
 // SIMD.  The row's Lc scale multiplies the f32 sum, which is stored as f32 or
-// rounded to bf16 (round to nearest even).
+// rounded to bf16 (round to nearest even), with non-temporal stores.
 //
 // Blocks are ordered so that each XCD (every 8th block goes to the same one)
 // works through a contiguous run of tiles: a column tile's 256 KiB of weights
@@ -172,20 +172,43 @@ __global__ __launch_bounds__(kPThreads) void project_rows_kernel(const uint8_t* 
     // epilogue: register r of accumulator (i, j) is row wm + 32 i + 8 (r / 4) +
     // 4 g + r % 4 and column wn + 32 j + l32
     const bool cols_ok = n0 + wn < N;  // (N - n0 is a multiple of 128)
+    // The output is written once and not read back here: non-temporal stores
+    // (8% faster on 8,192 x 32,768 than plain ones).
     if constexpr (kF32) {
-        // 32 consecutive f32 (128 bytes) of one row per half-wave store
-        float* out = static_cast<float*>(out_v);
+        // 32 consecutive f32 (128 bytes) of one row per half-wave store.  The
+        // lane's 64 row scales (rows wm + 32 i + 8 q + 4 g + 0..3) are read
+        // at once; row lrow starts at out + (m0 + wm + lrow) * N + n0 + wn.
+        float4 sc4[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int lrow = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-                const int64_t m = m0 + wm + lrow;
-                const float sc = s_rs[wm + lrow];
-                if (m < n_rows && cols_ok)
+            for (int q = 0; q < 4; ++q) sc4[i][q] = *reinterpret_cast<const float4*>(&s_rs[wm + 32 * i + 8 * q + 4 * g]);
+        auto scale_of = [&](int i, int r) {
+            const float4 v = sc4[i][r >> 2];
+            return (r & 3) == 0 ? v.x : (r & 3) == 1 ? v.y : (r & 3) == 2 ? v.z : v.w;
+        };
+        float* const ob = static_cast<float*>(out_v) + (m0 + wm + 4 * g) * static_cast<int64_t>(N) + n0 + wn + l32;
+        auto store_all = [&](auto row_ok) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) out[m * N + n0 + wn + 32 * j + l32] = acc[i][j][r] * sc;
-            }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int urow = 32 * i + 8 * (r >> 2) + (r & 3);  // lrow - 4 g
+                    const float sc = scale_of(i, r);
+                    float* const p = ob + static_cast<int64_t>(urow) * N;
+                    if (row_ok(urow)) {
+                        __builtin_nontemporal_store(acc[i][0][r] * sc, p);
+                        __builtin_nontemporal_store(acc[i][1][r] * sc, p + 32);
+                    }
+                }
+        };
+        // no row or column of the wave's tile past the end (wave-uniform, so
+        // the stores of a whole tile run without per-row branches)
+        const bool full = m0 + kPM <= n_rows && n0 + 64 * (__builtin_amdgcn_readfirstlane(w) & 3) < N;
+        if (full)
+            store_all([](int) { return true; });
+        else
+            store_all([&](int urow) { return m0 + wm + urow + 4 * g < n_rows && cols_ok; });
     } else {
         // each wave's 128 x 64 bf16 tile goes through LDS (rows of 144 bytes)
         // so that it leaves as 16-byte stores, 8 rows of 128 bytes per
@@ -209,7 +232,8 @@ __global__ __launch_bounds__(kPThreads) void project_rows_kernel(const uint8_t* 
             const int lrow = 8 * q + (lane >> 3);
             const int64_t m = m0 + wm + lrow;
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + lrow * kPRow + 16 * (lane & 7));
-            if (m < n_rows && cols_ok) *reinterpret_cast<u32x4_t*>(out + m * N + n0 + wn + 8 * (lane & 7)) = v;
+            if (m < n_rows && cols_ok)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + m * N + n0 + wn + 8 * (lane & 7)));
         }
     }
 

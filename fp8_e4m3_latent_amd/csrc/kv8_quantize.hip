@@ -147,6 +147,14 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     const int64_t row0 =
         (static_cast<int64_t>(blockIdx.x) * kQuantWaves + (threadIdx.x >> 6)) * kRowsPerWave;
     if (row0 >= n_rows) return;
+    // destination rows, loaded first: a load where the codes are stored would
+    // add a dependent round trip at the end of the wave's chain
+    int64_t drow[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        const int64_t row = row0 + r < n_rows ? row0 + r : row0;
+        drow[r] = dst_rows ? dst_rows[row] : row;
+    }
     // producer: the positions are loaded before the rows, so that the
     // rotation factors (which need only them) are computed while the row
     // loads are in flight (vector loads complete in order)
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     for (int r = 0; r < kRowsPerWave; ++r) {
         const int64_t row = row0 + r;
         if (row >= n_rows) break;
-        const int64_t d = dst_rows ? dst_rows[row] : row;
+        const int64_t d = drow[r];
         uint32_t* out = reinterpret_cast<uint32_t*>(codes + d * kRowBytes);
         __builtin_nontemporal_store(encode4(a[r], inv[2 * r], finite[2 * r]), out + lane);
         __builtin_nontemporal_store(encode4(b[r], inv[2 * r], finite[2 * r]), out + 64 + lane);
@@ -292,8 +300,9 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quantize_rows_kernel(
     }
     if (dst_rows) {
         // rows 1.. of a scattered wave: one lane each
-        for (int r = 1; r < nw; ++r)
-            if (lane == r) reinterpret_cast<float2*>(scales)[dst_rows[row0 + r]] = sp;
+#pragma unroll
+        for (int r = 1; r < kRowsPerWave; ++r)
+            if (r < nw && lane == r) reinterpret_cast<float2*>(scales)[drow[r]] = sp;
     } else if (lane < nw) {
         reinterpret_cast<float2*>(scales)[row0 + lane] = sp;  // contiguous rows: one store
     }

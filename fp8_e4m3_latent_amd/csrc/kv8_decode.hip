@@ -73,6 +73,7 @@ constexpr int kTT = 32;                          // tokens per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 32 * kWaves;       // 128 query rows
+constexpr int64_t kUnitRrBlocks = 1024;           // 4 blocks per compute unit of MI355X
 constexpr int kNBuf = 3;                         // raw Lc, decoded and scale buffers each
 constexpr int kRcBufs = 4;                       // raw Rc buffers
 constexpr int kRawLcBytes = kTT * kKvLora;       // 16384: raw Lc codes of a tile
@@ -101,6 +102,7 @@ struct DecodeArgs {
     int16_t* part_o;   // [n_splits][B][QH][512] codes, O = code * o_scale
     float* part_ml;    // [n_splits][B][QH] RangeStat records (16 bytes each)
     const uint8_t* exps;  // block exponents [rows][18] of block-scaled rows
+    int unit_rr;          // block order: (sequence, range) units dealt to the XCDs in turn
 };
 
 // s_waitcnt with only the vector-memory counter limited (lgkm and exp free)
@@ -406,16 +408,31 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     const int g = lane >> 5;        // lane half
     const int l32 = lane & 31;
 
-    // Blocks are dealt round-robin to the 8 XCDs (block i to XCD i % 8);
-    // renumber them so that each XCD runs a contiguous run of logical blocks,
-    // i.e. all token ranges of the same sequences, which then share their
-    // query rows in that XCD's L2.
-    int bid = blockIdx.x;
-    if ((gridDim.x & 7) == 0) bid = (bid & 7) * static_cast<int>(gridDim.x >> 3) + (bid >> 3);
-    const int rb = bid % p.n_rb;
-    bid /= p.n_rb;
-    const int split = bid % p.n_splits;
-    const int b = bid / p.n_splits;
+    // Blocks are dealt round-robin to the 8 XCDs (block i to XCD i % 8).
+    int rb, split, b;
+    if (p.unit_rr) {
+        // Launches of many blocks per compute unit (ragged lengths): the
+        // (sequence, range) units go to the XCDs in turn, the row blocks of a
+        // unit stay together on one XCD (they read the same KV tiles, through
+        // its L2), and the range index skews the sequences, so that every XCD
+        // gets a mix of long, short and empty ranges.  Needs B * n_splits to
+        // be a multiple of 8 (unit k = 0 .. B * n_splits - 1 exactly once).
+        const int x = static_cast<int>(blockIdx.x & 7), j = static_cast<int>(blockIdx.x >> 3);
+        const int k = (j / p.n_rb) * 8 + x;
+        split = k / p.B;
+        b = (k % p.B + split) % p.B;
+        rb = j % p.n_rb;
+    } else {
+        // Renumber the blocks so that each XCD runs a contiguous run of
+        // logical blocks, i.e. all token ranges of the same sequences, which
+        // then share their query rows in that XCD's L2.
+        int bid = blockIdx.x;
+        if ((gridDim.x & 7) == 0) bid = (bid & 7) * static_cast<int>(gridDim.x >> 3) + (bid >> 3);
+        rb = bid % p.n_rb;
+        bid /= p.n_rb;
+        split = bid % p.n_splits;
+        b = bid / p.n_splits;
+    }
 
     const int row0 = rb * kRowsPerBlock;
     const int row = row0 + 32 * w + l32;
@@ -1510,6 +1527,10 @@ int launch_absorb_decode(const DecodeLaunch& d, hipStream_t stream, bool merge) 
         a.part_ml = reinterpret_cast<float*>(a.part_o + rows * kKvLora);
     }
     const int64_t blocks = static_cast<int64_t>(d.B) * a.n_splits * a.n_rb;
+    // from 4 blocks per compute unit on, the order that balances the XCDs
+    // (the headline-sized launches, one block per unit, keep the order that
+    // shares each sequence's queries within one XCD)
+    a.unit_rr = blocks >= kUnitRrBlocks && (static_cast<int64_t>(d.B) * a.n_splits) % 8 == 0;
     if (d.exps != nullptr)
         hipLaunchKernelGGL(absorb_decode_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
                            0, stream, a);

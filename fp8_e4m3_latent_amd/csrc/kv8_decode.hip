@@ -17,14 +17,17 @@
 //   s_Lc / 2^e); the Rc codes stay in the raw tile;
 //
 //   score pass  S^T[token, row] = dec(KV)[token, 0:576] . q[row, 0:576]
-//               36 MFMA 32x32x16 f16 per tile, A = fp16 Lc rows
-//               (ds_read_b128) and the Rc codes converted in registers, B =
-//               the wave's 32 query rows resident in VGPRs as fp16 (each row
-//               scaled by a power of two so its largest element sits in
-//               [2^12, 2^13): every bf16 element above 2^-27 of the row maximum
-//               is then exact in fp16); separate accumulators for the Lc (512)
-//               and Rc (64) columns so the two row scales are applied after the
-//               dot product;
+//               18 MFMA 32x32x64 fp8 per tile on the raw e4m3 codes (A,
+//               ds_read_b128 from the raw tile) and the wave's 32 query rows
+//               resident in VGPRs as two e4m3 terms q = hi + lo (B; each row
+//               divided by a power of two so its largest element sits in
+//               [2^7, 2^8): hi is the nearest e4m3 value, lo the nearest to the
+//               exact remainder, and hi + lo equals every bf16 element above
+//               2^-10 of the row maximum, the rest within 2^-18 of it);
+//               separate accumulators for the Lc (512) and Rc (64) columns so
+//               the two row scales are applied after the dot product (rows of
+//               block-scaled codes: the scaled MFMA applies each 32-value
+//               block's exponent relative to the row's largest);
 //
 //   softmax     per row, with weights 2^(c (x - m)), c = |softmax_scale| log2(e)
 //               (the sign of the softmax scale rides on the row scales); a lane
@@ -49,9 +52,9 @@
 //               ~1e-4, at the same MFMA rate, and every e4m3 value is exact in
 //               fp16.
 //
-// Both passes therefore run on fp16 MFMA: every e4m3 value and every
-// (row-scaled) bf16 query element is exact in fp16, so the score products are
-// the exact products of the dequantized cache and the queries.
+// The score products are therefore the exact products of the dequantized
+// cache and the (split) queries, and the context pass multiplies exact fp16
+// values of the codes.
 //
 // A block either writes the normalised output (one token range per
 // sequence) or a partial (O, reference score m, sum l) that the log-sum-exp
@@ -67,6 +70,10 @@ namespace {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kTT = 32;                          // tokens per tile
@@ -74,14 +81,14 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 32 * kWaves;       // 128 query rows
 constexpr int64_t kUnitRrBlocks = 1024;           // 4 blocks per compute unit of MI355X
-constexpr int kNBuf = 3;                         // raw Lc, decoded and scale buffers each
-constexpr int kRcBufs = 4;                       // raw Rc buffers
+constexpr int kRawBufs = 4;                      // raw Lc, raw Rc and copied scale buffers
+constexpr int kDecBufs = 2;                      // fp16 Lc tile and decoded scale buffers
 constexpr int kRawLcBytes = kTT * kKvLora;       // 16384: raw Lc codes of a tile
 constexpr int kRawRcBytes = kTT * kRope;         // 2048: raw Rc codes of a tile
 constexpr int kLcStride = 2 * kKvLora + 64;      // 1088: fp16 Lc row + padding
 constexpr int kLcBytes = kTT * kLcStride;        // 34816
 
-constexpr int kScoreAhead = 3;                   // score operand loads in flight
+constexpr int kScoreAhead = 2;                   // score K-steps loaded ahead
 constexpr int kCtxAhead = 3;                     // context operand loads in flight
 constexpr float kLazyLog2 = 15.0f;
 
@@ -186,6 +193,15 @@ __device__ __forceinline__ void copy_to_lds_b128_rc(const void* base, uint32_t n
                  : "v"(off), "s"(buffer_rsrc(base, nbytes)), "s"(lds)
                  : "memory", "m0");
 }
+// the same through a given resource, the source moved by a uniform byte
+// offset soff (not counted by the range check, which takes the lane offset
+// alone; the LDS destination does not move)
+__device__ __forceinline__ void copy_to_lds_b128_rsrc(i32x4_t rsrc, uint32_t off, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(off), "s"(rsrc), "s"(soff), "s"(lds)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void copy_to_lds_b32_rc(const void* base, uint32_t nbytes, uint32_t off,
                                                    uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
@@ -251,34 +267,99 @@ __device__ __forceinline__ float pair_max(float v) {
     return m;
 }
 
-// Score MFMAs with their accumulator pinned to VGPRs, leaving all 256 AGPRs to
-// the context accumulator.  An MFMA needs two wait states after a VALU
-// write of one of its operands, which the compiler does not insert for
-// inline assembly: the variants taking an operand converted by VALU
-// instructions (NOP = true) start with s_nop 1; the others take operands
-// loaded from LDS (the load's s_waitcnt orders them) or registers written
-// long before.  Back-to-back MFMAs on the same accumulator need no wait
-// state.  The first MFMA of a chain starts from a zero C operand.
-template <bool NOP>
-__device__ __forceinline__ void mfma_score_first(f32x16_t& acc, const f16x8_t& a,
-                                                 const f16x8_t& b) {
-    if constexpr (NOP)
-        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+// Score MFMAs (fp8 e4m3 A and B, 32 x 32 x 64) with their accumulator pinned
+// to VGPRs, leaving all 256 AGPRs to the context accumulator.  An MFMA needs
+// two wait states after a VALU write of one of its operands, which the
+// compiler does not insert for inline assembly; the score MFMAs take A from
+// LDS loads (the load's s_waitcnt orders them) and B (the queries) and the
+// block scales from registers written long before.  Back-to-back MFMAs on
+// the same accumulator need no wait state.  The first MFMA of a chain starts
+// from a zero C operand.
+//
+// Operand layout (32 x 32 x 64 fp8): lane l holds row l % 32 of A (column
+// l % 32 of B); its bytes 0-15 are K = 16 (l / 32) + i and its bytes 16-31
+// K = 32 + 16 (l / 32) + i, so each 32-value K block is bytes 0-15 (or
+// 16-31) of both lane halves.  The scaled form multiplies row r's K block j
+// by 2^(S - 127) for the byte S that lane 32 j + r selects in its scale
+// register.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_score8(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b) {
+    if constexpr (FIRST)
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
     else
-        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-template <bool NOP>
-__device__ __forceinline__ void mfma_score(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
-    if constexpr (NOP)
-        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-    else
-        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+// the same with A's blocks scaled by byte SEL of sa (B unscaled: sb holds
+// 127; both scale operands must be VGPRs)
+template <bool FIRST, int SEL>
+__device__ __forceinline__ void mfma_score8s(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b,
+                                             uint32_t sa, uint32_t sb) {
+#define KV8_MFMA8S(C, OPS) \
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, " C ", %3, %4 " OPS \
+                 : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb))
+    // (the first MFMA of a chain follows the VALU writes of the scale
+    // registers: two wait states)
+    if constexpr (FIRST) {
+        asm volatile("s_nop 1" ::: "memory");
+        if constexpr (SEL == 0) KV8_MFMA8S("0", "op_sel_hi:[0,0,0]");
+        else if constexpr (SEL == 1) KV8_MFMA8S("0", "op_sel:[1,0,0] op_sel_hi:[0,0,0]");
+        else if constexpr (SEL == 2) KV8_MFMA8S("0", "op_sel_hi:[1,0,0]");
+        else KV8_MFMA8S("0", "op_sel:[1,0,0] op_sel_hi:[1,0,0]");
+    } else {
+        if constexpr (SEL == 0) KV8_MFMA8S("%0", "op_sel_hi:[0,0,0]");
+        else if constexpr (SEL == 1) KV8_MFMA8S("%0", "op_sel:[1,0,0] op_sel_hi:[0,0,0]");
+        else if constexpr (SEL == 2) KV8_MFMA8S("%0", "op_sel_hi:[1,0,0]");
+        else KV8_MFMA8S("%0", "op_sel:[1,0,0] op_sel_hi:[1,0,0]");
+    }
+#undef KV8_MFMA8S
+}
+
+// Two e4m3 terms of 8 bf16 query elements q (one per code byte, in element
+// order): hi = RNE_e4m3(q / qs) and lo = RNE_e4m3((q - hi qs) / qs), where qs
+// is a power of two and q / qs <= 256.  q - hi qs is exact in f32; hi + lo
+// equals q / qs whenever the remainder is an e4m3 value (every element with
+// q / qs >= 2^-2), and is within 2^-10 of it otherwise.
+__device__ __forceinline__ f32x2_t fp8x2_lo_to_f32(uint32_t w, float s) {
+    f32x2_t r;  // bytes 0, 1 times s
+    asm("v_cvt_scalef32_pk_f32_fp8 %0, %1, %2" : "=v"(r) : "v"(w), "v"(s));
+    return r;
+}
+__device__ __forceinline__ f32x2_t fp8x2_hi_to_f32(uint32_t w, float s) {
+    f32x2_t r;  // bytes 2, 3 times s
+    asm("v_cvt_scalef32_pk_f32_fp8 %0, %1, %2 op_sel:[1,0,0]" : "=v"(r) : "v"(w), "v"(s));
+    return r;
+}
+__device__ __forceinline__ void split_q8(uint4 q, float qs, uint2& hi, uint2& lo) {
+    const uint32_t x[4] = {q.x, q.y, q.z, q.w};
+    i16x2_t h[2] = {{0, 0}, {0, 0}}, l[2] = {{0, 0}, {0, 0}};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2_t v = __builtin_bit_cast(bf16x2_t, x[i]);
+        const float qa = __uint_as_float(x[i] << 16), qb = __uint_as_float(x[i] & 0xFFFF0000u);
+        f32x2_t hb;
+        if (i & 1) {
+            h[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(h[i >> 1], v, qs, true);
+            hb = fp8x2_hi_to_f32(__builtin_bit_cast(uint32_t, h[i >> 1]), qs);
+            l[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l[i >> 1], qa - hb.x, qb - hb.y, qs, true);
+        } else {
+            h[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(h[i >> 1], v, qs, false);
+            hb = fp8x2_lo_to_f32(__builtin_bit_cast(uint32_t, h[i >> 1]), qs);
+            l[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l[i >> 1], qa - hb.x, qb - hb.y, qs, false);
+        }
+    }
+    hi = make_uint2(__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]));
+    lo = make_uint2(__builtin_bit_cast(uint32_t, l[0]), __builtin_bit_cast(uint32_t, l[1]));
 }
 
 // Context MFMA with the accumulator pinned to AGPRs; its operands are the
 // packed probabilities (written before the phase starts) and LDS loads.
 __device__ __forceinline__ void mfma_ctx(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// the same after two wait states (its B operand was just converted by VALU
+// instructions)
+__device__ __forceinline__ void mfma_ctx_nop(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Wait states between the last MFMA on an accumulator and the first VALU read
@@ -339,16 +420,6 @@ __device__ __forceinline__ uint32_t absmax2_bf16x2(uint32_t m, uint32_t w) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// 8 bf16 values times 2^-k -> 8 fp16 values (exact for the scaled range)
-__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 q, int k) {
-    uint4 r;
-    r.x = pack_f16x2(__builtin_ldexpf(bf16_lo(q.x), -k), __builtin_ldexpf(bf16_hi(q.x), -k));
-    r.y = pack_f16x2(__builtin_ldexpf(bf16_lo(q.y), -k), __builtin_ldexpf(bf16_hi(q.y), -k));
-    r.z = pack_f16x2(__builtin_ldexpf(bf16_lo(q.z), -k), __builtin_ldexpf(bf16_hi(q.z), -k));
-    r.w = pack_f16x2(__builtin_ldexpf(bf16_lo(q.w), -k), __builtin_ldexpf(bf16_hi(q.w), -k));
-    return r;
-}
-
 template <typename T>
 __device__ __forceinline__ T lds_load(const uint8_t* base, int off) {
     return *reinterpret_cast<const T*>(base + off);
@@ -368,34 +439,37 @@ __device__ __forceinline__ f16x8_t ctx_operand(const uint8_t* lc, int tb0, int t
 }
 
 // LDS layouts of a tile (32 tokens t; chunks are 16 bytes):
-//   raw Lc  codes of t, chunk q (< 32), at chunk 32 t + (q ^ 8 ((t >> 2) & 1));
+//   raw Lc  codes of t, chunk c (< 32), at chunk 32 c + (t ^ 4 (c & 1));
 //   raw Rc  codes of t, chunk c (< 4), at chunk 32 c + t.  The tile copies
 //           place the chunks there (each lane picks its source chunk).
 //   fp16   Lc values of t, chunk c (< 64), at byte 1088 t + 16 (c ^ ((t >> 2) & 3)).
 // With 64 LDS banks of 4 bytes every read and write below touches each bank
-// once per 256 bytes: the score operand reads (16 tokens, one chunk each),
-// the transpose reads (4 tokens x 64 bytes per 32 lanes), the decode reads
-// (tokens t and t + 4) and writes (tokens t and t + 4, both chunk parities).
+// once per 256 bytes: the score operand reads and the decode reads (16
+// tokens, one chunk each), the byte transpose reads of the context operand
+// (8 tokens x 16 bytes per 16 lanes, two chunk parities per 32 lanes), the
+// fp16 transpose reads (4 tokens x 64 bytes per 32 lanes) and the decode
+// writes (16 tokens, one fp16 chunk each).
 
 // kMX: block-scaled rows (e4m3 codes with one ue8m0 exponent per 32 values).
 // Each token's largest Lc and Rc block exponents E_L, E_R take the place of
-// the per-row scales (s = 2^(E - 127)), and its codes are decoded to fp16
-// times 2^(E_block - E_L) (or - E_R): exact for blocks within 2^15 of their
-// segment's largest, smaller blocks round to fp16 subnormals.  The tile's
-// exponent bytes (576) are copied where the per-row path copies its scale
-// pairs (256), and the Rc codes cycle through three buffers instead of four
-// to make room.
+// the per-row scales (s = 2^(E - 127)).  The score MFMAs scale each block by
+// 2^(E_block - E_L) (or - E_R) exactly; the context pass decodes the Lc codes
+// to fp16 times 2^(E_block - E_L): exact for blocks within 2^15 of the row's
+// largest, smaller blocks round to fp16 subnormals.  The tile's exponent
+// bytes (576) are copied where the per-row path copies its scale pairs (256).
 template <bool kMX>
 __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p) {
-    constexpr int kRcB = kMX ? 3 : kRcBufs;                  // raw Rc buffers
     // copied scales, or exponents (576 bytes from byte 0 or 2 of a 4-byte word)
     constexpr int kScBytes = kMX ? kMxTileExpBytes + 16 : 8 * kTT;
-    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kNBuf][kRawLcBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_rc[kRcB][kRawRcBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_lc[kNBuf][kLcBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_scb[kNBuf][kScBytes];  // copied (Lc, Rc) scales or exponents
-    __shared__ __attribute__((aligned(16))) float s_scd[kNBuf][3 * kTT];  // s_Lc, s_Rc, s_Lc / 2^e
-    auto rc_buf = [](int tile) { return kMX ? tile % kRcB : tile & (kRcBufs - 1); };
+    // Raw buffers past kRawBufs - 1 only stage the queries (and keep the rope
+    // query terms); the fp16 Lc tiles exist for block-scaled rows only (the
+    // per-row path reads the context operand from the raw codes).
+    constexpr int kRawArr = kMX ? kRawBufs + 1 : 2 * kRawBufs + 1;
+    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawArr][kRawLcBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_rc[kRawBufs][kRawRcBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_lc[kMX ? kDecBufs : 1][kMX ? kLcBytes : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_scb[kRawBufs][kScBytes];  // copied (Lc, Rc) scales or exponents
+    __shared__ __attribute__((aligned(16))) float s_scd[kDecBufs][3 * kTT];  // s_Lc, s_Rc, s_Lc / 2^e
     __shared__ uint32_t s_red[3][kWaves];
     __shared__ int s_restart, s_shift;
     // per-row output factors of the epilogue, in the first raw Lc buffer (no
@@ -502,10 +576,11 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      read back in operand order once they have landed.  Lane l of the
     //      copy of row j takes the row's 16-byte chunk l ^ (j % 16), so that
     //      the 16 rows of a read fall on different banks.  The staging areas
-    //      are the fp16 tile buffers (waves 0-2) and raw buffers 1 and 2
-    //      (wave 3), all free until the first tile is decoded.  The rope
-    //      parts (128 bytes a row) load directly.
-    const uint8_t* const q_stage = w < kNBuf ? &s_lc[w][0] : &s_raw[0][0] + kRawLcBytes;
+    //      are raw buffers 2 w + 1 and 2 w + 2 (block-scaled rows: the fp16
+    //      tile buffers for waves 0 and 1, raw buffers 1-2 and 3-4 for waves
+    //      2 and 3), all free until tiles 1 and 2 are issued.  The rope parts
+    //      (128 bytes a row) load directly.
+    const uint8_t* const q_stage = !kMX ? &s_raw[2 * w + 1][0] : (w < kDecBufs ? &s_lc[w][0] : &s_raw[2 * w - 3][0]);
     {
         // (offsets from the sequence's first row: below 2^31, Q*H <= 2^21)
         const uint8_t* q_seq = reinterpret_cast<const uint8_t*>(p.q_lat + static_cast<int64_t>(b) * p.QH * kKvLora);
@@ -518,12 +593,13 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                              lds0 + 1024 * j);
         }
     }
+    // (qv[4 k + u]: chunk u of the query elements of score K-step k, below)
     uint4 qv[36];
     {
         const int64_t qrow = static_cast<int64_t>(b) * p.QH + (row_ok ? row : 0);
         const uint4* qr = reinterpret_cast<const uint4*>(p.q_rope + qrow * kRope);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) qv[32 + r] = qr[4 * g + r];
+        for (int u = 0; u < 4; ++u) qv[32 + u] = qr[2 * g + (u & 1) + 4 * (u >> 1)];
     }
 
 
@@ -531,39 +607,50 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      the 16 bytes of lane l land at chunk 64 i + l of the raw Lc buffer
     //      (i < 16) or at chunk 64 (i - 16) + l of the raw Rc buffer, whose
     //      source chunk (token, offset in the token's row) follows the raw
-    //      layouts.  Copy k < 4 (Lc) takes token 2 w + lane / 32 + 8 k, whose
-    //      chunk swizzle does not depend on k; copy 4 (i = 16, 17) takes Rc
-    //      chunk 2 (i - 16) + lane / 32 of token lane % 32.
-    auto dma_tl = [&](int ln) { return 2 * w + (ln >> 5); };  // token of the wave's Lc copy 0
-    auto dma_lc = [&](int ln) {
-        return dma_tl(ln) * kRowBytes + 16 * ((ln & 31) ^ (8 * ((dma_tl(ln) >> 2) & 1)));
-    };
+    //      layouts: chunk 2 i + lane / 32 of token (lane % 32) ^ (4 (lane /
+    //      32)) (Lc copy i < 16; the lane offset is the same for every copy,
+    //      copy i's 32 i bytes go into the base) and Rc chunk 2 (i - 16) +
+    //      lane / 32 of token lane % 32 (copy 4 of waves 0 and 1).
+    auto dma_lc = [&](int ln) { return ((ln & 31) ^ (4 * (ln >> 5))) * kRowBytes + 16 * (ln >> 5); };
     auto dma_rc = [&](int ln) { return (ln & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (ln >> 5)); };
     // The copies of a tile: tile i goes to raw Lc and scale buffer lbuf
     // (= i % 3) and raw Rc buffer i % 4.  Copy slot k < 4 of wave w is its Lc
-    // copy k; slot 4 is the Rc copy of wave w (waves 0 and 1) or the tile's 32
-    // (Lc, Rc) scale pairs, 4 bytes per lane (wave 3): waves 0, 1 and 3 issue
-    // five copies per tile, wave 2 four.  Tiles past the range are replaced
-    // by the last tile (a harmless re-copy into free buffers).  The copies
-    // are range-checked at the range's end: rows past it arrive as zero codes
-    // and zero scales (masked tokens, whose weight is 0).  The per-lane byte
-    // offsets do not depend on the tile; copy k's first row (8 k) goes into
-    // the base.
-    auto issue_copy = [&](int tile, int lbuf, int k, int ln) {
-        const int rbuf = rc_buf(tile);  // (before the clamp)
+    // copy w + 4 k; slot 4 is the Rc copy of wave w (waves 0 and 1) or the
+    // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (wave 3): waves 0, 1
+    // and 3 issue five copies per tile, wave 2 four.  Tiles past the range
+    // are replaced by the last tile (a harmless re-copy into free buffers).
+    // The copies are range-checked at the range's end: rows past it arrive as
+    // zero codes and zero scales (masked tokens, whose weight is 0).  The
+    // per-lane byte offsets do not depend on the tile.
+    // A tile's code rows: one buffer resource (its first row, valid rows x
+    // 576 bytes) for all its code copies.
+    struct TileSrc {
+        int64_t t0;
+        int valid;
+        i32x4_t rsrc;
+    };
+    auto tile_src = [&](int tile) {
         tile = tile < ntiles ? tile : ntiles - 1;
-        const int64_t t0 = ts + static_cast<int64_t>(tile) * kTT;
-        const uint8_t* base = p.codes + (row_base + t0) * kRowBytes;
-        const int valid = static_cast<int>(te - t0 < kTT ? te - t0 : kTT);  // (uniform, >= 1)
-        if (k < 4) {
-            const int rows = valid - 8 * k > 0 ? valid - 8 * k : 0;
-            copy_to_lds_b128_rc(base + 8 * k * kRowBytes, static_cast<uint32_t>(rows * kRowBytes),
-                                static_cast<uint32_t>(dma_lc(ln)),
-                                lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
+        TileSrc ts_;
+        ts_.t0 = ts + static_cast<int64_t>(tile) * kTT;
+        ts_.valid = static_cast<int>(te - ts_.t0 < kTT ? te - ts_.t0 : kTT);  // (uniform, >= 1)
+        ts_.rsrc = buffer_rsrc(p.codes + (row_base + ts_.t0) * kRowBytes, static_cast<uint32_t>(ts_.valid * kRowBytes));
+        return ts_;
+    };
+    const uint32_t lc_off = static_cast<uint32_t>(dma_lc(lane) + 32 * w);  // (Lc copy k: source + 128 k)
+    auto issue_copy = [&](const TileSrc& src, int lbuf, auto kc, int ln) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < 4) {
+            // Lc copy i = w + 4 k: lane offsets o = 576 t + 16 (lane / 32) +
+            // 32 w from the tile's first row, moved by 128 k; the range check
+            // o < 576 valid holds exactly for the tokens t < valid (whatever
+            // the lane's token)
+            copy_to_lds_b128_rsrc(src.rsrc, lc_off, 128 * k, lds_addr(&s_raw[lbuf][1024 * (w + kWaves * k)]));
         } else if (w < 2) {
-            copy_to_lds_b128_rc(base, static_cast<uint32_t>(valid * kRowBytes),
-                                static_cast<uint32_t>(dma_rc(ln)), lds_addr(&s_rc[rbuf][1024 * w]));
+            copy_to_lds_b128_rsrc(src.rsrc, static_cast<uint32_t>(dma_rc(ln)), 0, lds_addr(&s_rc[lbuf][1024 * w]));
         } else if (w == 3) {
+            const int64_t t0 = src.t0;
+            const int valid = src.valid;
             if constexpr (kMX) {
                 // the tile's 576 exponent bytes, 16 per lane on lanes 0-35; the
                 // range check counts whole dwords, so the last one may carry
@@ -582,12 +669,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // (outside the tile loop, with offsets rebuilt from a fresh lane id)
     auto issue_tile = [&](int tile) {
         const int ln = fresh_lane_id();
-#pragma unroll
-        for (int k = 0; k < 5; ++k) issue_copy(tile, tile % kNBuf, k, ln);
+        const TileSrc src = tile_src(tile);
+        static_for<5>([&](auto kc) { issue_copy(src, tile % kRawBufs, kc, ln); });
     };
 
-    // the first tile is in flight with the queries (tiles 1 and 2 go to
-    // buffers that stage the queries)
+    // the first tile is in flight with the queries (tiles 1-3 go to buffers
+    // that stage the queries)
     if (ntiles > 0) issue_tile(0);
 
     // ---- the range's largest Lc scale, largest Rc scale and smallest Lc
@@ -637,17 +724,23 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         }
     }
 
-    // ---- query row l32 of this wave: B operand of the score MFMA, fp16 after
-    //      scaling the row by 2^-kq so that its largest magnitude lies in
-    //      [2^12, 2^13): every bf16 element above 2^-27 of the row maximum
-    //      converts exactly.  Lc k-step ks holds columns 16 ks + 8 g .. +8;
-    //      Rc k-step r holds rope columns 32 g + 8 r .. +8 (the Rc operand
-    //      below takes the same order).  Rows past Q*H (block padding) reuse
-    //      row 0; their results are never stored.
+    // ---- query row l32 of this wave: B operand of the score MFMA, two e4m3
+    //      terms of the row divided by 2^kq so that its largest magnitude lies
+    //      in [2^7, 2^8).  Score K-step k < 8 of lane half g holds the Lc
+    //      columns 64 k + 16 g + [0, 16) (bytes 0-15) and 64 k + 32 + 16 g +
+    //      [0, 16) (bytes 16-31), K-step 8 the rope columns 16 g + [0, 16) and
+    //      32 + 16 g + [0, 16): the order of the cache codes in the A operand
+    //      below, and each 32-column block of the row is one K block of the
+    //      MFMA.  Rows past Q*H (block padding) reuse row 0; their results are
+    //      never stored.
     wait_all_copies();  // (the queries, tile 0 and the scale loads)
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks)
-        qv[ks] = lds_load<uint4>(q_stage, 1024 * l32 + 16 * ((2 * ks + g) ^ (l32 & 15)));
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = 8 * k + 2 * g + (u & 1) + 4 * (u >> 1);  // bf16 chunk of 8 columns
+            qv[4 * k + u] = lds_load<uint4>(q_stage, 1024 * l32 + 16 * (c ^ (l32 & 15)));
+        }
     int kq = 0;
     {
         uint32_t m2 = 0;
@@ -658,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         const uint32_t mbits = max(m2 << 16, m2 & 0xFFFF0000u);  // (f32 bits)
         const float qmax = fmaxf(__uint_as_float(mbits), other_half(__uint_as_float(mbits)));
         if (qmax > 0.0f) {
-            kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 12;
+            kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 7;
             kq = kq < -100 ? -100 : (kq > 120 ? 120 : kq);
         }
     }
@@ -704,35 +797,82 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         issue_tile(1);
         issue_tile(2);
     }
+    {
+        const float qs = __builtin_ldexpf(1.0f, kq);
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-        pin(qv[ks].x); pin(qv[ks].y); pin(qv[ks].z); pin(qv[ks].w);
-        qv[ks] = bf16x8_to_f16(qv[ks], kq);
+        for (int k = 0; k < 9; ++k) {
+            uint2 hi[4], lo[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pin(qv[4 * k + u].x); pin(qv[4 * k + u].y); pin(qv[4 * k + u].z); pin(qv[4 * k + u].w);
+                split_q8(qv[4 * k + u], qs, hi[u], lo[u]);
+                order();  // (one chunk at a time: its f32 temporaries stay few)
+            }
+            qv[4 * k + 0] = make_uint4(hi[0].x, hi[0].y, hi[1].x, hi[1].y);
+            qv[4 * k + 1] = make_uint4(hi[2].x, hi[2].y, hi[3].x, hi[3].y);
+            qv[4 * k + 2] = make_uint4(lo[0].x, lo[0].y, lo[1].x, lo[1].y);
+            qv[4 * k + 3] = make_uint4(lo[2].x, lo[2].y, lo[3].x, lo[3].y);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {  // (computed here, not next to their uses)
+                pin(qv[4 * k + u].x); pin(qv[4 * k + u].y); pin(qv[4 * k + u].z); pin(qv[4 * k + u].w);
+            }
+        }
     }
+    // The rope K-step's two terms (64 bytes a lane) wait in the staging-only
+    // raw buffer (4 KiB a wave, lane l at 16 (l + 64 i) for 16-byte part i),
+    // read back for each tile's first two score MFMAs: 16 fewer registers
+    // for the rest of the tile.  (Every wave has read its staged queries: the
+    // barrier after the staged reads.)
+    uint8_t* const q_rope_lds = &s_raw[kRawBufs][4096 * w] + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(q_rope_lds + 1024 * i) = qv[32 + i];
+    auto q_term = [&](int k, int t) {  // term t (0: hi, 1: lo) of Lc K-step k
+        const uint4 a = qv[4 * k + 2 * t], c = qv[4 * k + 2 * t + 1];
+        i32x8_t r;
+        r[0] = static_cast<int>(a.x); r[1] = static_cast<int>(a.y);
+        r[2] = static_cast<int>(a.z); r[3] = static_cast<int>(a.w);
+        r[4] = static_cast<int>(c.x); r[5] = static_cast<int>(c.y);
+        r[6] = static_cast<int>(c.z); r[7] = static_cast<int>(c.w);
+        return r;
+    };
 
     // ---- per-lane LDS offsets
-    // score A operand, Lc k-step ks: token l32, chunk 2 ks + g
-    const int hsw = (l32 >> 2) & 3;
-    const int sc_base0 = l32 * kLcStride + 16 * (g ^ hsw);        // ks even (+64 (ks >> 1))
-    const int sc_base1 = l32 * kLcStride + 16 * ((2 + g) ^ hsw);  // ks odd
-    // score A operand, Rc: token l32, chunks 2 g and 2 g + 1
-    // (token l32, chunks 2 g and 2 g + 1: byte 16 lane of the raw Rc layout)
+    // score A operand, K-step k: token l32, raw chunks 4 k + g (bytes 0-15)
+    // and 4 k + 2 + g (bytes 16-31), at byte 512 c + 16 (l32 ^ 4 g) (the
+    // rope K-step reads Rc chunks g and 2 + g at 512 c + 16 l32)
+    const int sc_base = 16 * (l32 ^ (4 * g)) + 512 * g;
+    const int sr_base = 16 * l32 + 512 * g;
+    // Offsets of phase B (context and decode), rebuilt from a fresh lane id at
+    // every phase B for block-scaled rows, whose phase A needs the registers.
     // context B operand: lane (G = lane / 16, gi = lane % 16) of k-group g
     // takes token 4 g + 8 h + gi / 4 (+ 16 kc) at dims 32 dt + 16 (G % 2) +
-    // 4 (gi % 4) for its transpose load h
-    const int G = lane >> 4, gi = lane & 15;
-    const int cG = 2 * (G & 1) + ((gi & 3) >> 1);
-    const int tb0 = (4 * g + (gi >> 2)) * kLcStride + 16 * (cG ^ (g & 3)) + 8 * (gi & 1);
-    const int tb1 = (4 * g + 8 + (gi >> 2)) * kLcStride + 16 * (cG ^ ((g + 2) & 3)) + 8 * (gi & 1);
-    // decode: lane 16 a + 8 bb + s of wave w converts token 8 w + a + 4 bb,
-    // raw chunks 8 j + s (j < 4) into fp16 chunks 16 j + 2 s, 16 j + 2 s + 1
-    const int d_bb = (lane >> 3) & 1, d_s = lane & 7;
-    const int d_t = 8 * w + (lane >> 4) + 4 * d_bb;
-    // (raw chunk 8 j + s sits at 8 (j ^ bb) + s; fp16 chunk 2 s + 1 is
-    //  chunk 2 s with bit 4 of the byte offset flipped)
-    const int d_rA = 512 * d_t + 16 * d_s + 128 * d_bb;         // j = 0, 2 (+256); j odd: ^ 128
-    const int d_hs = (d_t >> 2) & 3;
-    const int d_wA = d_t * kLcStride + 16 * ((2 * d_s) ^ d_hs);  // + 256 j; odd chunk: ^ 16
+    // 4 (gi % 4) for its transpose load h (h = 1: 8 tokens on, the chunk
+    // swizzle (g + 2) & 3 = g ^ 2 flips bit 5 of the byte offset)
+    // decode: lane (token l32, half g) of wave w converts the raw chunks c =
+    // 4 (2 w + g) + j (j < 4) of its token into fp16 chunks 2 c + e (e < 2):
+    // reads at byte 512 c + 16 (l32 ^ 4 (c & 1)), writes at byte 1088 l32 +
+    // 16 ((2 c + e) ^
+    // ((l32 >> 2) & 3)) = (d_wA ^ (32 (j % 2) + 16 e)) + 64 (j / 2)
+    // per-row context operand: lane L of group q addresses byte 512 c + 16
+    // (t ^ 4 (c & 1)) + 8 (L % 2) of chunk c = 2 (n % 16) + q % 2 and token t
+    // = 16 (n / 16) + 8 (L / 8) + 4 (q / 2) + (L / 2) % 4, which is c8_base +
+    // 1024 (n % 16) + 256 (n / 16)
+    int tb0 = 0, tb1 = 0, d_rA = 0, d_wA = 0, c8_base = 0;
+    auto phase_b_offsets = [&](int ln) {
+        const int lb = ln & 31, gb = ln >> 5;
+        if constexpr (kMX) {
+            const int G = ln >> 4, gi = ln & 15;
+            const int cG = 2 * (G & 1) + ((gi & 3) >> 1);
+            tb0 = (4 * gb + (gi >> 2)) * kLcStride + 16 * (cG ^ gb) + 8 * (gi & 1);
+            tb1 = (tb0 + 8 * kLcStride) ^ 32;
+            d_rA = 2048 * (2 * w + gb) + 16 * lb;  // + 512 j (odd j: ^ 64)
+            d_wA = lb * kLcStride + 128 * (2 * w + gb) + 16 * ((lb >> 2) & 3);
+        } else {
+            const int q = ln >> 4, L = ln & 15;
+            c8_base = 512 * (q & 1) + 128 * (L >> 3) + 64 * ((q >> 1) ^ (q & 1)) + 16 * ((L >> 1) & 3) + 8 * (L & 1);
+        }
+    };
+    phase_b_offsets(lane);
 
     // Scores x are kept in accumulator units times sgn = sign(c) / 2^ex (the
     // row scales carry the sign and are divided by 2^ex, so |x| < 2^32 for
@@ -759,61 +899,40 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     for (int dt = 0; dt < 16; ++dt) zero_acc(O[dt]);
 
     // ---- pipeline stages --------------------------------------------------
+    // Tile i's raw Lc codes, raw Rc codes and copied scales (or block
+    // exponents) live in s_raw / s_rc / s_scb [i % kRawBufs], its fp16 Lc tile
+    // and decoded scales in s_lc / s_scd [i % kDecBufs].
+    //
     // decode(tile): raw codes -> fp16 Lc tile, scales -> (s_Lc, s_Rc, s_Lc/2^e)
     uint4 draw[2];
-    auto decode_load = [&](int buf, int j) {  // raw chunk 8 j + s
-        const uint8_t* raw = &s_raw[buf][0];
-        draw[j & 1] = lds_load<uint4>(raw, ((j & 1) ? (d_rA ^ 128) : d_rA) + 256 * (j >> 1));
+    auto decode_load = [&](int rbuf, int j) {  // raw chunk 4 (2 w + g) + j of token l32
+        draw[j & 1] = lds_load<uint4>(&s_raw[rbuf][0], ((j & 1) ? (d_rA ^ 64) : d_rA) + 512 * j);
     };
-    // block-scaled rows: for the lane's four Lc blocks 4 j + s / 2 (s = lane
-    // % 8; the token's 8 lanes cover its 16 blocks) the exponent relative to
-    // the token's largest, E_block - E_L >= -128 as a signed byte j of
-    // mx_pack (below 2^-128 the fp16 value is 0 either way)
-    uint32_t mx_pack = 0;
-    auto mx_prep = [&](int buf) {
-        if constexpr (kMX) {
-            // (the lane's token and block rebuilt from a fresh lane id, so that
-            // no offset stays live across the tile loop)
-            const int ln = fresh_lane_id();
-            const int tok = 8 * w + (ln >> 4) + 4 * ((ln >> 3) & 1);
-            const uint8_t* ex = &s_scb[buf][mx_shift + kMxBlocksPerRow * tok + ((ln & 7) >> 1)];
-            int b[4];
-            uint32_t m = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b[j] = ex[4 * j];
-                m = max(m, static_cast<uint32_t>(b[j]));
-            }
-            m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x4E, 0xF, 0xF, false)));
-            m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), 0x141, 0xF, 0xF, false)));
-            mx_pack = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = b[j] - static_cast<int>(m);
-                mx_pack |= (static_cast<uint32_t>(d < -128 ? -128 : d) & 0xFFu) << (8 * j);
-            }
-        }
-    };
-    auto decode_store = [&](int buf, int j, int half) {
-        uint8_t* lc = &s_lc[buf][0];
+    // block-scaled rows: the exponents of the lane's two Lc blocks (raw chunks
+    // j = 0, 1 and j = 2, 3) relative to the token's largest, E_block - E_L
+    // >= -128 as signed bytes 2 and 3 of mx_sa[2] (below 2^-128 the fp16
+    // value is 0 either way); set with the score's block scales (mx_scales)
+    uint32_t mx_sa[3] = {0u, 0u, 0u};
+    auto decode_store = [&](int dbuf, int j, int half) {
+        uint8_t* lc = &s_lc[dbuf][0];
         const uint4 r = draw[j & 1];
         uint4 v;
         if constexpr (kMX) {
-            const float f = __builtin_ldexpf(1.0f, static_cast<int>(mx_pack << (24 - 8 * j)) >> 24);
+            const float f = __builtin_ldexpf(1.0f, static_cast<int>(mx_sa[2] << (8 - 8 * (j >> 1))) >> 24);
             v = half == 0 ? dec8_f16s(r.x, r.y, f) : dec8_f16s(r.z, r.w, f);
         } else {
             v = half == 0 ? dec8_f16(r.x, r.y) : dec8_f16(r.z, r.w);
         }
-        *reinterpret_cast<uint4*>(lc + (half == 0 ? d_wA : (d_wA ^ 16)) + 256 * j) = v;
+        *reinterpret_cast<uint4*>(lc + (d_wA ^ (32 * (j & 1) + 16 * half)) + 64 * (j >> 1)) = v;
     };
     // (every wave writes the same values: lane t < 32 the signed s_Lc / 2^ex,
     // s_Rc / 2^ex of token t, lane 32 + t the value s_Lc / 2^e of token t,
     // twice)
-    auto decode_scales = [&](int buf, int tile) {
+    auto decode_scales = [&](int rbuf, int dbuf, int tile) {
         float2 sc;
         if constexpr (kMX) {
             // 2^(E_L - 127), 2^(E_R - 127) of token l32; zero past the range
-            const uint8_t* base = &s_scb[buf][0];
+            const uint8_t* base = &s_scb[rbuf][0];
             const int tok = fresh_lane_id() & 31;
             const int a = mx_shift + kMxBlocksPerRow * tok;
             const uint32_t rp = mx_rc_pair(base, a);
@@ -822,9 +941,9 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             sc.y = in ? mx_pow2(static_cast<int>(max(rp & 0xFFu, rp >> 8))) : 0.0f;
         } else {
             (void)tile;
-            sc = *reinterpret_cast<const float2*>(&s_scb[buf][8 * l32]);
+            sc = *reinterpret_cast<const float2*>(&s_scb[rbuf][8 * l32]);
         }
-        float* d = &s_scd[buf][0];
+        float* d = &s_scd[dbuf][0];
         const float v0 = __builtin_ldexpf(g == 0 ? sgn * sc.x : sc.x, g == 0 ? -ex : -e);
         const float v1 = g == 0 ? __builtin_ldexpf(sgn * sc.y, -ex) : v0;
         d[g == 0 ? l32 : 2 * kTT + l32] = v0;
@@ -833,9 +952,9 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
 
     // x(tile) = s_Lc accL + s_Rc accR for row l32 and tokens 8 (j / 4) + 4 g +
     // j % 4 of the tile (the accumulator order), masked past the row's limit.
-    // The token scales of the lane's 16 tokens are loaded into registers
-    // during the score MFMAs (s_Rc, s_Lc) and before the accumulator drain
-    // (s_Lc / 2^e), so that the softmax does not wait on LDS.
+    // The token scales of the lane's 16 tokens are loaded into registers a
+    // group ahead of their use (s_Lc, s_Rc when x is formed, s_Lc / 2^e for
+    // P'), so that the arithmetic does not wait on LDS.
     float x[16];
     f32x16_t accL, accR;
     float4 sl4[4], sr4[4], se4[4];
@@ -866,174 +985,251 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         }
     };
 
-    // score(tile): accR = dec(Rc) . q_rope (4 MFMAs, first), then accL =
-    // dec(Lc) . q_lat (32 MFMAs); step ks < 36 issues one MFMA so that other
-    // work can sit between the steps.  The Rc codes of the lane's token are
-    // loaded before the phase (rope_load) and converted one MFMA ahead.
-    f16x8_t aq[kScoreAhead];
-    uint4 rope[2];
-    f16x8_t ropeop;
-    float mx_rf = 1.0f;  // block-scaled rows: 2^(E of Rc block g - E_R) of the lane's token
-    auto rope_load = [&](int tile) {
-        const uint8_t* rc = &s_rc[rc_buf(tile)][0];
-        const int ln = fresh_lane_id();
-        const int rope_off = 16 * (ln + (ln & 32));  // (= 16 (64 g + l32))
-        rope[0] = lds_load<uint4>(rc, rope_off);
-        rope[1] = lds_load<uint4>(rc, rope_off + 16 * 32);
+    // score(tile): the rope K-step into accR first, then the Lc K-steps 0-7
+    // into accL, two MFMAs (query terms hi, lo) per K-step; step s < 18
+    // issues one MFMA so that other work can sit between the steps.  K-step q
+    // of that order (0: rope, 1 + k: Lc k) is loaded kScoreAhead K-steps
+    // ahead.
+    i32x8_t aq[kScoreAhead];
+    auto score_load = [&](int rbuf, int q) {
+        const uint8_t* base = q == 0 ? &s_rc[rbuf][0] : &s_raw[rbuf][0] + 2048 * (q - 1);
+        const int o = q == 0 ? sr_base : sc_base;
+        const uint4 x = lds_load<uint4>(base, o), y = lds_load<uint4>(base, o + 1024);
+        i32x8_t r;
+        r[0] = static_cast<int>(x.x); r[1] = static_cast<int>(x.y);
+        r[2] = static_cast<int>(x.z); r[3] = static_cast<int>(x.w);
+        r[4] = static_cast<int>(y.x); r[5] = static_cast<int>(y.y);
+        r[6] = static_cast<int>(y.z); r[7] = static_cast<int>(y.w);
+        aq[q % kScoreAhead] = r;
+    };
+    // block-scaled rows: lane (token l32, half g) scales K block g of every
+    // K-step: Lc block 2 k + g (byte k % 4 of mx_sa[k / 4]) and Rc block g
+    // (byte 0 of mx_sa[2]), each by E_block - E_max + 127 (at least 0) for
+    // the token's largest Lc (Rc) block exponent E_max
+    const uint32_t mx_sb = 0x7F7F7F7Fu;  // (the queries unscaled)
+    auto mx_scales = [&](int rbuf) {
         if constexpr (kMX) {
-            const uint32_t rp = mx_rc_pair(&s_scb[tile % kNBuf][0], mx_shift + kMxBlocksPerRow * (ln & 31));
-            const int eg = static_cast<int>((ln & 32) ? rp >> 8 : rp & 0xFFu);
-            mx_rf = __builtin_ldexpf(1.0f, eg - static_cast<int>(max(rp & 0xFFu, rp >> 8)));
-        }
-    };
-    auto rope_operand = [&](int r) {
-        const uint4 c4 = rope[r >> 1];
-        if constexpr (kMX)
-            ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16s(c4.z, c4.w, mx_rf) : dec8_f16s(c4.x, c4.y, mx_rf));
-        else
-            ropeop = __builtin_bit_cast(f16x8_t, (r & 1) ? dec8_f16(c4.z, c4.w) : dec8_f16(c4.x, c4.y));
-    };
-    auto score_begin = [&](int buf) {
-        const uint8_t* lc = &s_lc[buf][0];
+            const int ln = fresh_lane_id();
+            const int a = mx_shift + kMxBlocksPerRow * (ln & 31);
+            const uint32_t* d = reinterpret_cast<const uint32_t*>(&s_scb[rbuf][0] + (a & ~3));
+            const uint32_t sh = 8 * (a & 3);  // (0 or 16)
+            uint32_t v[4];
+            uint32_t m = 0;
 #pragma unroll
-        for (int k = 0; k < kScoreAhead; ++k)
-            aq[k] = lds_load<f16x8_t>(lc, (k & 1 ? sc_base1 : sc_base0) + 64 * (k >> 1));
-        rope_operand(0);
-    };
-    auto score_step = [&](int buf, int ks) {
-        const uint8_t* lc = &s_lc[buf][0];
-        if (ks < 4) {
-            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[32 + ks]);
-            if (ks == 0) mfma_score_first<true>(accR, ropeop, qb);
-            else mfma_score<true>(accR, ropeop, qb);
-            if (ks < 3) rope_operand(ks + 1);
-        } else {
-            const int kl = ks - 4;
-            const f16x8_t a = aq[kl % kScoreAhead];
-            const int kn = kl + kScoreAhead;
-            if (kn < 32) aq[kl % kScoreAhead] = lds_load<f16x8_t>(lc, (kn & 1 ? sc_base1 : sc_base0) + 64 * (kn >> 1));
-            const f16x8_t qb = __builtin_bit_cast(f16x8_t, qv[kl]);
-            if (kl == 0) mfma_score_first<false>(accL, a, qb);
-            else mfma_score<false>(accL, a, qb);
+            for (int i = 0; i < 4; ++i) {
+                v[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);  // Lc bytes 4 i .. 4 i + 3
+                m = max(m, max(max(v[i] & 0xFFu, (v[i] >> 8) & 0xFFu), max((v[i] >> 16) & 0xFFu, v[i] >> 24)));
+            }
+            const uint32_t rp = (d[4] >> sh) & 0xFFFFu;  // Rc bytes 16, 17
+            const uint32_t mr = max(rp & 0xFFu, rp >> 8);
+            const uint32_t gsh = 8 * static_cast<uint32_t>(ln >> 5);
+            auto rel = [](uint32_t e, uint32_t mm) {
+                const int r = static_cast<int>(e) - static_cast<int>(mm) + 127;
+                return static_cast<uint32_t>(r < 0 ? 0 : r);
+            };
+            uint32_t s0 = 0, s1 = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                // block 2 k + g: byte 2 (k % 2) + g of v[k / 2]
+                const uint32_t e = (v[k >> 1] >> (16 * (k & 1) + gsh)) & 0xFFu;
+                if (k < 4) s0 |= rel(e, m) << (8 * k);
+                else s1 |= rel(e, m) << (8 * (k - 4));
+            }
+            mx_sa[0] = s0;
+            mx_sa[1] = s1;
+            mx_sa[2] = rel((rp >> gsh) & 0xFFu, mr);
+            // the decode's blocks 4 w + 2 g and 4 w + 2 g + 1: bytes 2 g and
+            // 2 g + 1 of v[w] (w uniform)
+            const uint32_t vw = w == 0 ? v[0] : (w == 1 ? v[1] : (w == 2 ? v[2] : v[3]));
+            const int d0 = static_cast<int>((vw >> (2 * gsh)) & 0xFFu) - static_cast<int>(m);
+            const int d1 = static_cast<int>((vw >> (2 * gsh + 8)) & 0xFFu) - static_cast<int>(m);
+            mx_sa[2] |= ((static_cast<uint32_t>(d0 < -128 ? -128 : d0) & 0xFFu) << 16) |
+                        ((static_cast<uint32_t>(d1 < -128 ? -128 : d1) & 0xFFu) << 24);
+            // (all computed here: nothing of the exponent bytes stays live)
+            pin(mx_sa[0]); pin(mx_sa[1]); pin(mx_sa[2]);
         }
+    };
+    i32x8_t qr[2];  // the rope K-step's query terms, for the first two MFMAs
+    auto score_begin = [&](int rbuf) {
+        mx_scales(rbuf);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint4 x = lds_load<uint4>(q_rope_lds, 2048 * t), y = lds_load<uint4>(q_rope_lds, 2048 * t + 1024);
+            qr[t][0] = static_cast<int>(x.x); qr[t][1] = static_cast<int>(x.y);
+            qr[t][2] = static_cast<int>(x.z); qr[t][3] = static_cast<int>(x.w);
+            qr[t][4] = static_cast<int>(y.x); qr[t][5] = static_cast<int>(y.y);
+            qr[t][6] = static_cast<int>(y.z); qr[t][7] = static_cast<int>(y.w);
+        }
+#pragma unroll
+        for (int q = 0; q < kScoreAhead; ++q) score_load(rbuf, q);
+    };
+    auto score_step = [&](int rbuf, int st) {
+        const int q = st >> 1, t = st & 1;  // K-step q, query term t
+        const i32x8_t a = aq[q % kScoreAhead];
+        const i32x8_t qb = q == 0 ? qr[t] : q_term(q - 1, t);
+        if constexpr (kMX) {
+            const uint32_t sa = mx_sa[q == 0 ? 2 : (q - 1) >> 2];
+            const int sel = q == 0 ? 0 : (q - 1) & 3;
+            f32x16_t& acc = q == 0 ? accR : accL;
+            const bool first = t == 0 && q <= 1;
+            if (first) mfma_score8s<true, 0>(acc, a, qb, sa, mx_sb);
+            else if (sel == 0) mfma_score8s<false, 0>(acc, a, qb, sa, mx_sb);
+            else if (sel == 1) mfma_score8s<false, 1>(acc, a, qb, sa, mx_sb);
+            else if (sel == 2) mfma_score8s<false, 2>(acc, a, qb, sa, mx_sb);
+            else mfma_score8s<false, 3>(acc, a, qb, sa, mx_sb);
+        } else {
+            if (q == 0) {
+                if (t == 0) mfma_score8<true>(accR, a, qb);
+                else mfma_score8<false>(accR, a, qb);
+            } else {
+                if (q == 1 && t == 0) mfma_score8<true>(accL, a, qb);
+                else mfma_score8<false>(accL, a, qb);
+            }
+        }
+        if (t == 1 && q + kScoreAhead < 9) score_load(rbuf, q + kScoreAhead);
     };
 
-    // softmax(tile) in steps k < kSoftSteps of a few VALU instructions each,
-    // so that they can sit between the context MFMAs of the previous tile:
-    //   0-8    even k: x of token group k / 2 - 1 (k > 0), then the loads of
-    //          s_Lc and s_Rc for group k / 2 (k < 8); one group of scales in
-    //          flight at a time
-    //   9-10   mask (tiles past the first visible-token limit) and the maximum
-    //          of the lane's 16 scores
-    //   11     the row maximum (with the other half of the wave)
-    //   12     reference update
-    //   13-20  p = 2^(c_row (x - ref) + dsh) for tokens 2 (k - 13) and
-    //          2 (k - 13) + 1
-    //   21-24  lsum = sum of the p (pairwise), loads of s_Lc / 2^e for token
-    //          group k - 21
-    //   25-28  P' = p s_Lc / 2^e for token group k - 25, and the lane's largest
-    //          P' of the real tiles
-    //   29-30  P' packed to fp16 as the A operand of context k-step k - 29
-    constexpr int kSoftSteps = 31;
-    uint4 pa[2], pn[2];  // P' of the tile in the context MFMAs, and of the next
+    // x(tile) in 9 steps (phase B, after the scales of the tile are decoded):
+    // even step 2 q4 forms the scores of token group q4 - 1 (q4 > 0) and
+    // loads the scales s_Lc, s_Rc of group q4 (q4 < 4); one group of scales
+    // in flight at a time
+    auto fx_step = [&](int k, int dbuf) {
+        if (k % 2 == 1) return;
+        const int q4 = k / 2;
+        if (q4 > 0) {
+            form_x(q4 - 1);
+            pin(x[4 * q4 - 4]); pin(x[4 * q4 - 3]); pin(x[4 * q4 - 2]); pin(x[4 * q4 - 1]);
+        }
+        if (q4 < 4) {
+            scales_load_l(dbuf, q4);
+            scales_load_r(dbuf, q4);
+        }
+    };
+    // softmax(tile) in steps k < kSoftSteps of a few VALU instructions each
+    // (phase A, between the score MFMAs of the next tile), from the scores x:
+    //   0      mask (tiles past the first visible-token limit), maxima of
+    //          three triples of the lane's 16 scores
+    //   1      the lane's maximum
+    //   2      the row maximum (with the other half of the wave)
+    //   3      reference update
+    //   4-11   p = 2^(c_row (x - ref) + dsh) for tokens 2 (k - 4) and
+    //          2 (k - 4) + 1
+    //   12-15  lsum = sum of the p (pairwise)
+    //   16-19  P' = p s_Lc / 2^e for token group k - 16 (its scales loaded by
+    //          se_load two steps before), and the lane's largest P'
+    //   20-21  P' packed to fp16 as the A operand of context k-step k - 20
+    constexpr int kSoftSteps = 22;
+    uint4 pa[2];  // P' of the tile, the A operand of its context MFMAs
     float mx_part = 0.0f, mx_pair = 0.0f, ref = 0.0f, lsum = 0.0f;
     float mxa = 0.0f, mxb = 0.0f, mxc = 0.0f, sum_t[8];
     bool restart = false;  // this lane's row raised its reference in this pass
-    auto soft_step = [&](int k, int buf, int tile, bool real) {
-        if (k < 9) {
-            if (k % 2 == 1) return;
-            const int q4 = k / 2;
-            if (q4 > 0) {
-                form_x(q4 - 1);
-                pin(x[4 * q4 - 4]); pin(x[4 * q4 - 3]); pin(x[4 * q4 - 2]); pin(x[4 * q4 - 1]);
-            }
-            if (q4 < 4) {
-                scales_load_l(buf, q4);
-                scales_load_r(buf, q4);
-            }
-            return;
-        }
-        k -= 5;
-        if (k == 4) {
+    auto soft_step = [&](int k, int tile) {
+        if (k == 0) {
             mask_x(tile);
             mxa = max3(x[0], x[1], x[2]);
             mxb = max3(x[3], x[4], x[5]);
             mxc = max3(x[6], x[7], x[8]);
             pin(mxa); pin(mxb); pin(mxc);
-        } else if (k == 5) {
+        } else if (k == 1) {
             const float d = max3(x[9], x[10], x[11]);
             const float f = max3(x[12], x[13], x[14]);
             mx_part = fmaxf(max3(mxa, mxb, mxc), max3(d, f, x[15]));
             pin(mx_part);
-        } else if (k == 6) {
+        } else if (k == 2) {
             mx_pair = pair_max(mx_part);
             pin(mx_pair);
-        } else if (k == 7) {
+        } else if (k == 3) {
             const float mx = mx_pair;
             const bool first = m_x == mask_val;  // nothing accumulated for this row yet
             const bool raise = !first && c_row * (mx - m_x) > kLazyLog2;
-            m_x = real && (first || raise) ? mx : m_x;
-            restart = restart || (real && raise);
+            m_x = first || raise ? mx : m_x;
+            restart = restart || raise;
             ref = m_x == mask_val ? 0.0f : m_x;
             pin(ref);
-        } else if (k < 16) {
-            const int j = 2 * (k - 8);
+        } else if (k < 12) {
+            const int j = 2 * (k - 4);
             pin(x[j]); pin(x[j + 1]);
             x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(c_row, x[j] - ref, dsh));
             x[j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(c_row, x[j + 1] - ref, dsh));
             pin(x[j]); pin(x[j + 1]);
-        } else if (k < 18) {
-            scales_load_e(buf, k - 16);
-            const int j0 = 4 * (k - 16);
+        } else if (k < 14) {
+            const int j0 = 4 * (k - 12);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sum_t[j0 + i] = x[2 * (j0 + i)] + x[2 * (j0 + i) + 1];
                 pin(sum_t[j0 + i]);
             }
-        } else if (k == 18) {
-            scales_load_e(buf, 2);
+        } else if (k == 14) {
             sum_t[0] = (sum_t[0] + sum_t[1]) + (sum_t[2] + sum_t[3]);
             sum_t[4] = (sum_t[4] + sum_t[5]) + (sum_t[6] + sum_t[7]);
             pin(sum_t[0]); pin(sum_t[4]);
-        } else if (k == 19) {
-            scales_load_e(buf, 3);
+        } else if (k == 15) {
             lsum = sum_t[0] + sum_t[4];
             pin(lsum);
-        } else if (k < 24) {
-            const int q4 = k - 20;
+        } else if (k < 20) {
+            const int q4 = k - 16;
             pin(x[4 * q4]); pin(x[4 * q4 + 1]); pin(x[4 * q4 + 2]); pin(x[4 * q4 + 3]);
             x[4 * q4 + 0] *= se4[q4].x;
             x[4 * q4 + 1] *= se4[q4].y;
             x[4 * q4 + 2] *= se4[q4].z;
             x[4 * q4 + 3] *= se4[q4].w;
-            {
-                const float t = max3(max3(pmax, x[4 * q4], x[4 * q4 + 1]), x[4 * q4 + 2], x[4 * q4 + 3]);
-                pmax = real ? t : pmax;
-            }
+            pmax = max3(max3(pmax, x[4 * q4], x[4 * q4 + 1]), x[4 * q4 + 2], x[4 * q4 + 3]);
             pin(x[4 * q4]); pin(x[4 * q4 + 1]); pin(x[4 * q4 + 2]); pin(x[4 * q4 + 3]);
         } else {
-            const int kc = k - 24;
-            pn[kc].x = pack_f16x2(x[8 * kc + 0], x[8 * kc + 1]);
-            pn[kc].y = pack_f16x2(x[8 * kc + 2], x[8 * kc + 3]);
-            pn[kc].z = pack_f16x2(x[8 * kc + 4], x[8 * kc + 5]);
-            pn[kc].w = pack_f16x2(x[8 * kc + 6], x[8 * kc + 7]);
-            pin(pn[kc].x); pin(pn[kc].y); pin(pn[kc].z); pin(pn[kc].w);
+            const int kc = k - 20;
+            pa[kc].x = pack_f16x2(x[8 * kc + 0], x[8 * kc + 1]);
+            pa[kc].y = pack_f16x2(x[8 * kc + 2], x[8 * kc + 3]);
+            pa[kc].z = pack_f16x2(x[8 * kc + 4], x[8 * kc + 5]);
+            pa[kc].w = pack_f16x2(x[8 * kc + 6], x[8 * kc + 7]);
+            pin(pa[kc].x); pin(pa[kc].y); pin(pa[kc].z); pin(pa[kc].w);
         }
     };
 
     // context(tile): O[dt] += P (32 rows x 16 tokens) . dec(Lc) (16 tokens x
-    // 32 dims), 32 MFMAs, operand loads kCtxAhead MFMAs ahead
+    // 32 dims), 32 MFMAs n (dims 32 (n % 16) .., tokens 16 (n / 16) ..).
+    // Per-row path: the Lc operand comes straight from the raw codes: a byte
+    // transpose load (ds_read_b64_tr_b8) gives lane t of each 16-lane group
+    // byte t % 8 of the 8 bytes of lanes 2 j + t / 8 (j < 8), so lane 2 j + h
+    // of group q addresses the codes of dims 16 (q % 2) + 8 h .. + 7 of the
+    // token of MFMA K index j of lane half q / 2 (token 8 (j / 4) + 4 (q / 2)
+    // + j % 4 of the 16, the order of the probabilities), and four exact
+    // conversions make the fp16 operand.  Raw loads run three MFMAs ahead,
+    // conversions one.  Block-scaled rows read the fp16 tile (two fp16
+    // transpose loads per operand, kCtxAhead MFMAs ahead).
     f16x8_t bq[kCtxAhead];
+    uint2 craw[3];
+    auto ctx8_load = [&](int rbuf, int n) {
+        const uint8_t* a = &s_raw[rbuf][0] + c8_base + 1024 * (n & 15) + 256 * (n >> 4);
+        typedef int i32x2_t __attribute__((ext_vector_type(2)));
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(a));
+        craw[n % 3] = make_uint2(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]));
+    };
+    auto ctx8_convert = [&](int n) {
+        const uint2 r = craw[n % 3];
+        bq[n & 1] = __builtin_bit_cast(f16x8_t, dec8_f16(r.x, r.y));
+    };
     auto context_begin = [&](int buf) {
-        const uint8_t* lc = &s_lc[buf][0];
+        if constexpr (kMX) {
+            const uint8_t* lc = &s_lc[buf][0];
 #pragma unroll
-        for (int n = 0; n < kCtxAhead; ++n) bq[n] = ctx_operand(lc, tb0, tb1, n);
+            for (int n = 0; n < kCtxAhead; ++n) bq[n] = ctx_operand(lc, tb0, tb1, n);
+        } else {
+#pragma unroll
+            for (int n = 0; n < 3; ++n) ctx8_load(buf, n);
+            ctx8_convert(0);
+        }
     };
     auto context_step = [&](int buf, int n, uint4 pk) {
-        const uint8_t* lc = &s_lc[buf][0];
-        const f16x8_t bv = bq[n % kCtxAhead];
-        if (n + kCtxAhead < 32) bq[n % kCtxAhead] = ctx_operand(lc, tb0, tb1, n + kCtxAhead);
-        mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bv);
+        if constexpr (kMX) {
+            const uint8_t* lc = &s_lc[buf][0];
+            const f16x8_t bv = bq[n % kCtxAhead];
+            if (n + kCtxAhead < 32) bq[n % kCtxAhead] = ctx_operand(lc, tb0, tb1, n + kCtxAhead);
+            mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bv);
+        } else {
+            mfma_ctx_nop(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bq[n & 1]);
+            if (n + 3 < 32) ctx8_load(buf, n + 3);
+            if (n + 1 < 32) ctx8_convert(n + 1);
+        }
     };
 
     if (tid == 0) {
@@ -1046,112 +1242,111 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // finishes (so every reference ends within kLazyLog2 of every tile
     // maximum) and the range is then run once more from a zero accumulator.
     //
-    // Software pipeline (tile i): copy(i) is issued four tiles ahead and
-    // waited for at the end of the next iteration, decode(i) runs two tiles
-    // ahead; iteration i runs
-    //   phase A: score(i + 1), with the decode of tile i + 2 between its
-    //            MFMAs
-    //   phase B: context(i), with the softmax steps of tile i + 1 between its
-    //            MFMAs (the P' they pack feeds context(i + 1))
-    // and the five copy slots of tile i + 4 spread over both phases (a burst
-    // of copies stalls their issue while earlier misses are outstanding)
-    // and one barrier, after the copies of tile i + 3 have landed.  Stages
-    // past the last tile run on stale buffers and their results are never
-    // used.
+    // Software pipeline: the copies of tile i are issued three tiles ahead
+    // into raw buffers i % 4 (free once tile i - 4 has passed its context
+    // pass) and waited for at the end of iteration i - 2; iteration i runs
+    //   phase A: score(i + 1) from its raw codes, with the softmax of tile i
+    //            (its scores x were formed last iteration), three copies of
+    //            tile i + 3 and (block-scaled rows) the decode of tile i + 1
+    //            into an fp16 Lc tile between its MFMAs
+    //   phase B: context(i) with the P' of that softmax (from tile i's raw
+    //            codes, or its fp16 tile), with the scales and scores x of
+    //            tile i + 1 and two copies of tile i + 3 between its MFMAs
+    // and one barrier, after the copies of tile i + 2 have landed (those of
+    // tile i + 3 stay in flight).  Stages past the last tile run on
+    // re-copies of the last tile and their results are never used.
     auto end_barrier = [&]() {
         if (w == 2) barrier_after_copies<4>();
         else barrier_after_copies<5>();
+    };
+    // the decode of tile `tile` (raw buffers rb, fp16 buffers db), spread
+    // over the steps n < 16 of a phase
+    auto decode_step = [&](auto nc, int rb, int db) {
+        constexpr int n = decltype(nc)::value;
+        if constexpr (kMX && n % 4 == 0 && n < 16) decode_load(rb, n / 4);
+        if constexpr (kMX && n % 4 == 2 && n < 16) decode_store(db, n / 4, 0);
+        if constexpr (kMX && n % 4 == 3 && n < 16) decode_store(db, n / 4, 1);
+    };
+    // the scales of tile `tile` and its scores x, over steps n < 11
+    auto scores_step = [&](auto nc, int rb, int db, int tile) {
+        constexpr int n = decltype(nc)::value;
+        if constexpr (n == 0) decode_scales(rb, db, tile);
+        if constexpr (n >= 2 && n < 11) fx_step(n - 2, db);
     };
     // One pass over the token range (every pass also records each lane's
     // largest probability operand, which only a watched pass reads).
     auto run_pass = [&]() {
         if (ntiles > 0) {
-            mx_prep(0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                decode_load(0, j);
-                decode_store(0, j, 0);
-                decode_store(0, j, 1);
-            }
-            decode_scales(0, 0);
-            end_barrier();  // tile 0 decoded; tile 1 landed, tile 2 may be in flight
-            if constexpr (kMX) {
-                // (tile 3's Rc codes and exponents reuse tile 0's buffers)
-                rope_load(0);
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                issue_tile(3);
-            } else {
-                issue_tile(3);  // (raw buffers of tile 0, decoded)
-                rope_load(0);
-            }
+            // tile 0 (landed; tiles 1 and 2 in flight): score, decode, scores x
             score_begin(0);
-            static_for<36>([&](auto kc) {
-                constexpr int ks = decltype(kc)::value;
-                score_step(0, ks);
-                // decode of tile 1 between the score MFMAs (as in phase A)
-                if constexpr (ks >= 6 && ks <= 30 && (ks - 6) % 8 == 0) decode_load(1, (ks - 6) / 8);
-                if constexpr (ks == 7) mx_prep(1);
-                if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(1, (ks - 9) / 8, 0);
-                if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(1, (ks - 11) / 8, 1);
-                if constexpr (ks == 35) decode_scales(1, 1);
+            static_for<18>([&](auto sc) {
+                score_step(0, decltype(sc)::value);
+                decode_step(sc, 0, 0);
             });
             mfma_acc_drain(accL, accR);
-            static_for<kSoftSteps>([&](auto k) { soft_step(decltype(k)::value, 0, 0, true); });
-            l_run += lsum;
-            pa[0] = pn[0];
-            pa[1] = pn[1];
-            // tile 1 decoded, tile 2 landed; tile 0's Rc codes are read before
-            // copy(4) reuses them
-            end_barrier();
+            static_for<11>([&](auto nc) { scores_step(nc, 0, 0, 0); });
+            end_barrier();  // tile 1 landed; tile 2 may be in flight
         }
-        // iteration `it` with R = it % kNBuf known at compile time, so that
+        // iteration `it` with R = it % kRawBufs known at compile time, so that
         // every LDS address is a lane offset plus an immediate
         auto iteration = [&](int it, auto rc) {
             constexpr int R = decltype(rc)::value;
-            constexpr int B0 = R, B1 = (R + 1) % kNBuf, B2 = (R + 2) % kNBuf;
-            const bool real_next = it + 1 < ntiles;
-            // ---------------- phase A: score(it + 1), decode of tile it + 2,
-            //                  copies of tile it + 4 into the buffers of tile
-            //                  it + 1 (raw Lc, scales: decoded last iteration)
-            //                  and tile it (raw Rc: scored last iteration)
-            rope_load(it + 1);
-            score_begin(B1);
+            constexpr int RN = (R + 1) % kRawBufs;                        // tile it + 1
+            constexpr int RC = (R + 3) % kRawBufs;                        // tile it + 3
+            constexpr int CB = kMX ? R % kDecBufs : R;  // context operand buffer (fp16 or raw)
+            constexpr int D0 = R % kDecBufs, D1 = (R + 1) % kDecBufs;
+            // ---------------- phase A: score(it + 1) (and decode) of tile it + 1
+            //                  from raw buffers RN, softmax of tile it (scales
+            //                  in D0), copies of tile it + 3 into the raw
+            //                  buffers of tile it - 1 (done with last
+            //                  iteration)
+            const TileSrc csrc = tile_src(it + 3);
+            score_begin(RN);
             order();
-            static_for<36>([&](auto kc) {
-                constexpr int ks = decltype(kc)::value;
-                score_step(B1, ks);
-                // decode of tile it + 2 between the score MFMAs (loads well
-                // ahead of their conversions and stores)
-                if constexpr (ks >= 6 && ks <= 30 && (ks - 6) % 8 == 0) decode_load(B2, (ks - 6) / 8);
-                if constexpr (ks == 7) mx_prep(B2);
-                if constexpr (ks >= 9 && ks <= 33 && (ks - 9) % 8 == 0) decode_store(B2, (ks - 9) / 8, 0);
-                if constexpr (ks >= 11 && ks <= 35 && (ks - 11) % 8 == 0) decode_store(B2, (ks - 11) / 8, 1);
-                if constexpr (ks == 35) decode_scales(B2, it + 2);
-                if constexpr (ks % 11 == 3) issue_copy(it + 4, B1, ks / 11, lane);
+            static_for<18>([&](auto sc) {
+                constexpr int st = decltype(sc)::value;
+                score_step(RN, st);
+                // softmax steps: one per MFMA, two at steps 12, 13, 16 and
+                // 17; the scales of P' loaded two MFMAs ahead of their use
+                if constexpr (st < 12) soft_step(st, it);
+                if constexpr (st == 12 || st == 13) {
+                    soft_step(2 * st - 12, it);
+                    soft_step(2 * st - 11, it);
+                }
+                if constexpr (st == 14 || st == 15) soft_step(st + 2, it);
+                if constexpr (st == 16 || st == 17) {
+                    soft_step(2 * st - 14, it);
+                    soft_step(2 * st - 13, it);
+                }
+                if constexpr (st >= 12 && st < 16) scales_load_e(D0, st - 12);
+                decode_step(sc, RN, D1);
+                if constexpr (st == 5 || st == 9 || st == 13)
+                    issue_copy(csrc, RC, std::integral_constant<int, (st - 5) / 4>{}, lane);
                 order();
             });
-            // ---------------- phase B: context(it) (it reads only buffers
-            //                  written before the last barrier), softmax of
-            //                  tile it + 1 (its result is only used when real)
-            context_begin(B0);
+            l_run += lsum;
+            // ---------------- phase B: context(it) from buffer CB (written
+            //                  before the last barrier), scales and scores x of
+            //                  tile it + 1
+            if constexpr (kMX) phase_b_offsets(fresh_lane_id());
+            context_begin(CB);
             order();
             static_for<32>([&](auto nc) {
                 constexpr int n = decltype(nc)::value;
-                context_step(B0, n, n < 16 ? pa[0] : pa[1]);
+                context_step(CB, n, n < 16 ? pa[0] : pa[1]);
                 if constexpr (n == 0) mfma_acc_drain(accL, accR);
-                if constexpr (n < kSoftSteps) soft_step(n, B1, it + 1, real_next);
-                if constexpr (n % 11 == 5 && n / 11 < 2) issue_copy(it + 4, B1, 3 + n / 11, lane);
+                if constexpr (n >= 12 && n < 23) scores_step(std::integral_constant<int, n - 12>{}, RN, D1, it + 1);
+                if constexpr (n == 5 || n == 25)
+                    issue_copy(csrc, RC, std::integral_constant<int, 3 + n / 16>{}, lane);
                 order();
             });
-            l_run += real_next ? lsum : 0.0f;
-            pa[0] = pn[0];
-            pa[1] = pn[1];
-            end_barrier();  // tile it + 3 landed; tile it + 4 may be in flight
+            end_barrier();  // tile it + 2 landed; tile it + 3 may be in flight
         };
-        for (int it0 = 0; it0 < ntiles; it0 += kNBuf) {
+        for (int it0 = 0; it0 < ntiles; it0 += kRawBufs) {
             iteration(it0, std::integral_constant<int, 0>{});
             if (it0 + 1 < ntiles) iteration(it0 + 1, std::integral_constant<int, 1>{});
             if (it0 + 2 < ntiles) iteration(it0 + 2, std::integral_constant<int, 2>{});
+            if (it0 + 3 < ntiles) iteration(it0 + 3, std::integral_constant<int, 3>{});
         }
     };
 

@@ -1193,20 +1193,24 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // of group q addresses the codes of dims 16 (q % 2) + 8 h .. + 7 of the
     // token of MFMA K index j of lane half q / 2 (token 8 (j / 4) + 4 (q / 2)
     // + j % 4 of the 16, the order of the probabilities), and four exact
-    // conversions make the fp16 operand.  Raw loads run three MFMAs ahead,
-    // conversions one.  Block-scaled rows read the fp16 tile (two fp16
+    // conversions make the fp16 operand.  Raw loads run kRawAhead MFMAs
+    // ahead and conversions two (an MFMA does not wait on the conversions of
+    // its own operand).  Block-scaled rows read the fp16 tile (two fp16
     // transpose loads per operand, kCtxAhead MFMAs ahead).
+    constexpr int kRawAhead = 4;
     f16x8_t bq[kCtxAhead];
-    uint2 craw[3];
+    uint2 craw[kRawAhead];
     auto ctx8_load = [&](int rbuf, int n) {
         const uint8_t* a = &s_raw[rbuf][0] + c8_base + 1024 * (n & 15) + 256 * (n >> 4);
         typedef int i32x2_t __attribute__((ext_vector_type(2)));
         const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(a));
-        craw[n % 3] = make_uint2(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]));
+        craw[n % kRawAhead] = make_uint2(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]));
     };
     auto ctx8_convert = [&](int n) {
-        const uint2 r = craw[n % 3];
-        bq[n & 1] = __builtin_bit_cast(f16x8_t, dec8_f16(r.x, r.y));
+        const uint2 r = craw[n % kRawAhead];
+        uint4 c = dec8_f16(r.x, r.y);
+        pin(c.x); pin(c.y); pin(c.z); pin(c.w);
+        bq[n % 2] = __builtin_bit_cast(f16x8_t, c);
     };
     auto context_begin = [&](int buf) {
         if constexpr (kMX) {
@@ -1215,8 +1219,9 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             for (int n = 0; n < kCtxAhead; ++n) bq[n] = ctx_operand(lc, tb0, tb1, n);
         } else {
 #pragma unroll
-            for (int n = 0; n < 3; ++n) ctx8_load(buf, n);
+            for (int n = 0; n < kRawAhead; ++n) ctx8_load(buf, n);
             ctx8_convert(0);
+            ctx8_convert(1);
         }
     };
     auto context_step = [&](int buf, int n, uint4 pk) {
@@ -1226,9 +1231,10 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             if (n + kCtxAhead < 32) bq[n % kCtxAhead] = ctx_operand(lc, tb0, tb1, n + kCtxAhead);
             mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bv);
         } else {
-            mfma_ctx_nop(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bq[n & 1]);
-            if (n + 3 < 32) ctx8_load(buf, n + 3);
-            if (n + 1 < 32) ctx8_convert(n + 1);
+            if (n < 2) mfma_ctx_nop(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bq[n % 2]);
+            else mfma_ctx(O[n & 15], __builtin_bit_cast(f16x8_t, pk), bq[n % 2]);
+            if (n + kRawAhead < 32) ctx8_load(buf, n + kRawAhead);
+            if (n + 2 < 32) ctx8_convert(n + 2);
         }
     };
 

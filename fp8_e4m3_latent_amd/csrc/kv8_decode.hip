@@ -11,19 +11,23 @@
 // range.  Wave w owns rows 32w..32w+31 for the whole computation:
 //
 //   tiles of 32 tokens are copied global -> LDS by direct-to-LDS loads three
-//   tiles ahead (three raw fp8 buffers); two tiles ahead, all 256 threads
-//   decode a raw tile once, exactly, into an fp16 Lc tile (three buffers,
-//   rows padded to 1088 bytes) and turn its scales into (s_Lc, s_Rc,
-//   s_Lc / 2^e); the Rc codes stay in the raw tile;
+//   tiles ahead (four buffers of raw Lc codes, Rc codes and scale pairs);
+//   both MFMA passes read the raw codes, and a tile's scale pairs become
+//   (s_Lc, s_Rc, s_Lc / 2^e) in LDS before its scores are formed (rows of
+//   block-scaled codes also decode their Lc codes one tile ahead into an
+//   fp16 tile, two buffers, each block times its exponent relative to the
+//   row's largest);
 //
 //   score pass  S^T[token, row] = dec(KV)[token, 0:576] . q[row, 0:576]
 //               18 MFMA 32x32x64 fp8 per tile on the raw e4m3 codes (A,
 //               ds_read_b128 from the raw tile) and the wave's 32 query rows
 //               resident in VGPRs as two e4m3 terms q = hi + lo (B; each row
 //               divided by a power of two so its largest element sits in
-//               [2^7, 2^8): hi is the nearest e4m3 value, lo the nearest to the
-//               exact remainder, and hi + lo equals every bf16 element above
-//               2^-10 of the row maximum, the rest within 2^-18 of it);
+//               [2^7, 2^8), or by 2^-126 for rows below 2^-119: hi is the
+//               nearest e4m3 value, lo the nearest to the exact remainder, and
+//               hi + lo equals every bf16 element of at least 2^-9 of the row
+//               maximum (every element of rows below 2^-119), the rest within
+//               2^-17 of it; a NaN or infinite element makes the row NaN);
 //               separate accumulators for the Lc (512) and Rc (64) columns so
 //               the two row scales are applied after the dot product (rows of
 //               block-scaled codes: the scaled MFMA applies each 32-value
@@ -44,8 +48,10 @@
 //   context     O[row, 0:512] += (p * s_Lc / 2^e)[row, token] . dec(Lc)[token, :]
 //               32 MFMA 32x32x16 f16 per tile; the probabilities come straight
 //               from the score accumulator registers (their token order is the
-//               MFMA K order), the Lc operand is read with the LDS transpose
-//               load ds_read_b64_tr_b16, and 2^e normalises the largest Lc
+//               MFMA K order), the Lc operand is read from the raw codes with
+//               the byte transpose load ds_read_b64_tr_b8 and converted
+//               exactly to fp16 in registers (block-scaled rows: fp16 transpose
+//               loads of the decoded tile), and 2^e normalises the largest Lc
 //               scale of the block's token range below 1 so p * s / 2^e fits
 //               fp16.  fp16 rather than bf16 carries the probabilities: one
 //               bf16 rounding of p already costs ~1e-3 of the output, fp16
@@ -315,10 +321,13 @@ __device__ __forceinline__ void mfma_score8s(f32x16_t& acc, const i32x8_t& a, co
 }
 
 // Two e4m3 terms of 8 bf16 query elements q (one per code byte, in element
-// order): hi = RNE_e4m3(q / qs) and lo = RNE_e4m3((q - hi qs) / qs), where qs
-// is a power of two and q / qs <= 256.  q - hi qs is exact in f32; hi + lo
-// equals q / qs whenever the remainder is an e4m3 value (every element with
-// q / qs >= 2^-2), and is within 2^-10 of it otherwise.
+// order): hi = RNE_e4m3(q / qs) and lo = RNE_e4m3(q / qs - hi), where qs is
+// a power of two (a normal float, inv = 1 / qs) and q / qs <= 256.  The
+// remainder q inv - hi is formed exactly by one fused multiply-add in the
+// scaled units (no f32 subnormal on the way, whatever the magnitude of q);
+// hi + lo equals q / qs whenever the remainder is an e4m3 value (every
+// element with q / qs >= 2^-2, and every bf16 value when qs = 2^-126), and is
+// within 2^-10 of it otherwise.  A NaN or infinite q gives a NaN hi.
 __device__ __forceinline__ f32x2_t fp8x2_lo_to_f32(uint32_t w, float s) {
     f32x2_t r;  // bytes 0, 1 times s
     asm("v_cvt_scalef32_pk_f32_fp8 %0, %1, %2" : "=v"(r) : "v"(w), "v"(s));
@@ -329,7 +338,7 @@ __device__ __forceinline__ f32x2_t fp8x2_hi_to_f32(uint32_t w, float s) {
     asm("v_cvt_scalef32_pk_f32_fp8 %0, %1, %2 op_sel:[1,0,0]" : "=v"(r) : "v"(w), "v"(s));
     return r;
 }
-__device__ __forceinline__ void split_q8(uint4 q, float qs, uint2& hi, uint2& lo) {
+__device__ __forceinline__ void split_q8(uint4 q, float qs, float inv, uint2& hi, uint2& lo) {
     const uint32_t x[4] = {q.x, q.y, q.z, q.w};
     i16x2_t h[2] = {{0, 0}, {0, 0}}, l[2] = {{0, 0}, {0, 0}};
 #pragma unroll
@@ -339,12 +348,14 @@ __device__ __forceinline__ void split_q8(uint4 q, float qs, uint2& hi, uint2& lo
         f32x2_t hb;
         if (i & 1) {
             h[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(h[i >> 1], v, qs, true);
-            hb = fp8x2_hi_to_f32(__builtin_bit_cast(uint32_t, h[i >> 1]), qs);
-            l[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l[i >> 1], qa - hb.x, qb - hb.y, qs, true);
+            hb = fp8x2_hi_to_f32(__builtin_bit_cast(uint32_t, h[i >> 1]), 1.0f);
+            l[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+                l[i >> 1], __builtin_fmaf(qa, inv, -hb.x), __builtin_fmaf(qb, inv, -hb.y), 1.0f, true);
         } else {
             h[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(h[i >> 1], v, qs, false);
-            hb = fp8x2_lo_to_f32(__builtin_bit_cast(uint32_t, h[i >> 1]), qs);
-            l[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l[i >> 1], qa - hb.x, qb - hb.y, qs, false);
+            hb = fp8x2_lo_to_f32(__builtin_bit_cast(uint32_t, h[i >> 1]), 1.0f);
+            l[i >> 1] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+                l[i >> 1], __builtin_fmaf(qa, inv, -hb.x), __builtin_fmaf(qb, inv, -hb.y), 1.0f, false);
         }
     }
     hi = make_uint2(__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]));
@@ -416,9 +427,6 @@ __device__ __forceinline__ uint32_t absmax2_bf16x2(uint32_t m, uint32_t w) {
                                                                   __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu)));
 }
 
-// bf16 bits -> f32
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 template <typename T>
 __device__ __forceinline__ T lds_load(const uint8_t* base, int off) {
@@ -578,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      the 16 rows of a read fall on different banks.  The staging areas
     //      are raw buffers 2 w + 1 and 2 w + 2 (block-scaled rows: the fp16
     //      tile buffers for waves 0 and 1, raw buffers 1-2 and 3-4 for waves
-    //      2 and 3), all free until tiles 1 and 2 are issued.  The rope parts
+    //      2 and 3), all free until tiles 1 to 3 are issued.  The rope parts
     //      (128 bytes a row) load directly.
     const uint8_t* const q_stage = !kMX ? &s_raw[2 * w + 1][0] : (w < kDecBufs ? &s_lc[w][0] : &s_raw[2 * w - 3][0]);
     {
@@ -613,8 +621,8 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //      lane / 32 of token lane % 32 (copy 4 of waves 0 and 1).
     auto dma_lc = [&](int ln) { return ((ln & 31) ^ (4 * (ln >> 5))) * kRowBytes + 16 * (ln >> 5); };
     auto dma_rc = [&](int ln) { return (ln & 31) * kRowBytes + kKvLora + 16 * (2 * (w & 1) + (ln >> 5)); };
-    // The copies of a tile: tile i goes to raw Lc and scale buffer lbuf
-    // (= i % 3) and raw Rc buffer i % 4.  Copy slot k < 4 of wave w is its Lc
+    // The copies of a tile: tile i goes to the raw Lc, Rc and scale buffers
+    // lbuf = i % 4.  Copy slot k < 4 of wave w is its Lc
     // copy w + 4 k; slot 4 is the Rc copy of wave w (waves 0 and 1) or the
     // tile's 32 (Lc, Rc) scale pairs, 4 bytes per lane (wave 3): waves 0, 1
     // and 3 issue five copies per tile, wave 2 four.  Tiles past the range
@@ -752,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         const float qmax = fmaxf(__uint_as_float(mbits), other_half(__uint_as_float(mbits)));
         if (qmax > 0.0f) {
             kq = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 7;
-            kq = kq < -100 ? -100 : (kq > 120 ? 120 : kq);
+            kq = kq < -126 ? -126 : (kq > 120 ? 120 : kq);  // (2^kq and 2^-kq normal floats)
         }
     }
 
@@ -798,14 +806,14 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         issue_tile(2);
     }
     {
-        const float qs = __builtin_ldexpf(1.0f, kq);
+        const float qs = __builtin_ldexpf(1.0f, kq), qinv = __builtin_ldexpf(1.0f, -kq);
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
             uint2 hi[4], lo[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 pin(qv[4 * k + u].x); pin(qv[4 * k + u].y); pin(qv[4 * k + u].z); pin(qv[4 * k + u].w);
-                split_q8(qv[4 * k + u], qs, hi[u], lo[u]);
+                split_q8(qv[4 * k + u], qs, qinv, hi[u], lo[u]);
                 order();  // (one chunk at a time: its f32 temporaries stay few)
             }
             qv[4 * k + 0] = make_uint4(hi[0].x, hi[0].y, hi[1].x, hi[1].y);
@@ -1105,7 +1113,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
             scales_load_r(dbuf, q4);
         }
     };
-    // softmax(tile) in steps k < kSoftSteps of a few VALU instructions each
+    // softmax(tile) in 22 steps k of a few VALU instructions each
     // (phase A, between the score MFMAs of the next tile), from the scores x:
     //   0      mask (tiles past the first visible-token limit), maxima of
     //          three triples of the lane's 16 scores
@@ -1118,7 +1126,6 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     //   16-19  P' = p s_Lc / 2^e for token group k - 16 (its scales loaded by
     //          se_load two steps before), and the lane's largest P'
     //   20-21  P' packed to fp16 as the A operand of context k-step k - 20
-    constexpr int kSoftSteps = 22;
     uint4 pa[2];  // P' of the tile, the A operand of its context MFMAs
     float mx_part = 0.0f, mx_pair = 0.0f, ref = 0.0f, lsum = 0.0f;
     float mxa = 0.0f, mxb = 0.0f, mxc = 0.0f, sum_t[8];
@@ -1535,8 +1542,10 @@ static_assert(sizeof(RangeStat) == 16, "partial statistics record");
 
 // out[b, row, :] = sum_s (w_s l_s / L) (O_s / l_s) over the ranges with
 // l_s > 0, w_s = 2^(c (m_s - m*)) with m* the reference of largest c m_s and
-// L = sum_s w_s l_s; zero when no range saw a token.  The weights are formed
-// before they meet the codes, so no intermediate leaves the float range.
+// L = sum_s w_s l_s; zero when no range saw a token, NaN when a range's sum
+// l_s is NaN (its query row has a NaN or infinite element).  The weights are
+// formed before they meet the codes, so no intermediate leaves the float
+// range.
 //
 // four 16-bit codes (two dwords, low half first) as floats
 __device__ __forceinline__ float4 codes4_to_f32(uint2 c) {
@@ -1587,10 +1596,16 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const int16_t*
     const double cabs = fabs(static_cast<double>(c));
 
     double kmax = -INFINITY;
-    for (int s = tid; s < n_splits; s += kMergeThreads) kmax = fmax(kmax, range_key(part_ml[s * stride + br], cpos));
+    int bad = 0;  // a NaN sum
+    for (int s = tid; s < n_splits; s += kMergeThreads) {
+        const RangeStat st = part_ml[s * stride + br];
+        kmax = fmax(kmax, range_key(st, cpos));
+        bad |= !(st.l >= 0.0f);
+    }
     kmax = wave_max_f64(kmax);
     if ((tid & 63) == 0) s_k[tid >> 6] = kmax;
     __syncthreads();
+    bad = __syncthreads_or(bad);
     kmax = fmax(fmax(s_k[0], s_k[1]), fmax(s_k[2], s_k[3]));
     float lsum = 0.0f;
     if (kmax > -INFINITY) {
@@ -1629,6 +1644,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const int16_t*
             const float4 v = s_acc[g2][q];
             a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
         }
+        if (bad) a = make_float4(NAN, NAN, NAN, NAN);
         *reinterpret_cast<float4*>(out + br * kKvLora + col0 + 4 * q) = a;
     }
 }
@@ -1647,6 +1663,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel
     const double cabs = fabs(static_cast<double>(c));
     RangeStat st{0.0, 0.0f, 0.0f};
     if (lane < n_splits) st = part_ml[lane * stride + br];
+    const bool bad = __any(!(st.l >= 0.0f));  // a NaN sum
     const double kmax = wave_max_f64(range_key(st, cpos));
     const float wgt = kmax > -INFINITY ? range_weight(st, cpos, cabs, kmax) : 0.0f;
     const float lsum = wave_sum_f32(wgt * st.l);
@@ -1676,6 +1693,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel
             a1.x += w2 * v1.x; a1.y += w2 * v1.y; a1.z += w2 * v1.z; a1.w += w2 * v1.w;
         }
     }
+    if (bad) a0 = a1 = make_float4(NAN, NAN, NAN, NAN);
     float* o = out + br * kKvLora + 8 * lane;
     *reinterpret_cast<float4*>(o) = a0;
     *reinterpret_cast<float4*>(o + 4) = a1;

@@ -161,10 +161,15 @@ int kv8_norm_rope_quantize_rows(const float* src, int64_t src_row_stride, int64_
  * scale_Lc[t] * dec(Lc_t).  Long sequences are split internally and merged
  * by log-sum-exp.
  *
- * Accuracy (every finite cache and query, any row magnitude): the score and
- * context products are exact products of the dequantized rows and the bf16
- * queries summed in f32; scores are formed relative to the largest row scale
- * of the token range, so they stay finite for rows up to the f32 maximum.
+ * Accuracy (every finite cache and query, any row magnitude): the score
+ * products are exact products of the dequantized rows and the queries,
+ * summed in f32, where each query row enters as two e4m3 terms whose sum
+ * equals every bf16 element of at least 2^-9 of the row's largest magnitude
+ * (every element of rows below 2^-119) and is within 2^-17 of that largest
+ * magnitude for the others; scores are formed relative to the largest row
+ * scale of the token range, so they stay finite for rows up to the f32
+ * maximum.  A query row with a NaN or infinite element gives a NaN output
+ * row (other rows are unaffected).
  * The probabilities enter the context pass as fp16 relative to the range's
  * largest Lc scale; a range whose Lc scales differ by more than 2^6 is run
  * watched, and a query row whose largest probability operand falls below

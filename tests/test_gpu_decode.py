@@ -151,6 +151,85 @@ def test_extreme_row_scales(kv8):
     run_case(kv8, w, splits=3, cache=cache)
 
 
+def test_query_rows_of_any_magnitude(kv8):
+    """Query rows of every bf16 magnitude.  The score MFMAs take each query
+    element as two e4m3 terms after dividing its row by a power of two; the
+    sum of the terms must reproduce the bf16 element (exactly for elements
+    of at least 2^-9 of the row's largest, and for every element of rows
+    below 2^-119, whose elements are then mostly bf16 subnormals).  Sequences
+    whose queries are scaled by 1e-37, 1e-30, 1e-6, 1e20 and 1e36 attend rows
+    scaled by the inverse, with softmax scale 1 so that the scores spread
+    over several natural-log units (a query error of 2^-10 would show), and
+    one sequence's query elements are 2^U(-40, 0) with random signs (most of
+    them below 2^-9 of their row's largest)."""
+    T = 300
+    mq = np.array([1e-37, 1e-30, 1e-6, 1.0, 1e20, 1e36, 1.0])
+    B = len(mq)
+    w = workloads.tiny(seed=41, B=B, Q=1, H=32, T=T, outlier_p=0.0)
+    ql = workloads.bf16_to_f32(w.q_lat).astype(np.float64)
+    qr = workloads.bf16_to_f32(w.q_rope).astype(np.float64)
+    rng = np.random.default_rng(42)
+    for b in range(B):
+        if b == B - 1:
+            mag = np.exp2(rng.uniform(-40.0, 0.0, size=ql[b].shape))
+            ql[b] = np.copysign(mag, ql[b])
+            mag = np.exp2(rng.uniform(-40.0, 0.0, size=qr[b].shape))
+            qr[b] = np.copysign(mag, qr[b])
+            mr = 0.5
+        else:
+            ql[b] *= mq[b]
+            qr[b] *= mq[b]
+            mr = 3.0 / mq[b]  # score std ~ 3 before the softmax scale
+        w.rows[b * T:(b + 1) * T] *= np.float32(mr)
+    w.q_lat = workloads.bf16_bits(ql.astype(np.float32))
+    w.q_rope = workloads.bf16_bits(qr.astype(np.float32))
+    assert np.all(np.isfinite(w.rows))
+    assert np.all(np.isfinite(workloads.bf16_to_f32(w.q_lat)))
+    w.softmax_scale = np.float32(1.0)
+    cache = build_cache(kv8, w.rows)
+    run_case(kv8, w, cache=cache)
+    run_case(kv8, w, splits=2, cache=cache)
+
+
+def test_non_finite_query_elements(kv8):
+    """A query row with one NaN, +inf or -inf element (latent or rope part)
+    gives an all-NaN output row, as the oracle's; every other row of the
+    same blocks matches the oracle.  Direct output and split partials."""
+    w = workloads.tiny(seed=43, B=2, Q=1, H=32, T=300, outlier_p=0.0)
+    ql = workloads.bf16_to_f32(w.q_lat)
+    qr = workloads.bf16_to_f32(w.q_rope)
+    bad = [(0, 3), (0, 9), (1, 4), (1, 31)]
+    ql[0, 0, 3, 17] = np.nan
+    ql[0, 0, 9, 500] = np.inf
+    qr[1, 0, 4, 5] = -np.inf
+    ql[1, 0, 31, 0] = np.nan
+    w.q_lat = workloads.bf16_bits(ql)
+    w.q_rope = workloads.bf16_bits(qr)
+    cache = build_cache(kv8, w.rows)
+    codes, scales, c, s = cache
+    ql_d, qr_d, st, ln = to_dev(w)
+    ref = oracle.attention(w.q_lat, w.q_rope, c, s, w.kv_start, w.kv_len, Q=w.Q,
+                           softmax_scale=w.softmax_scale).reshape(w.B, w.H, KL)
+    nan_rows = np.zeros((w.B, w.H), bool)
+    for b, h in bad:
+        nan_rows[b, h] = True
+    assert np.all(np.isnan(ref[nan_rows])) and np.all(np.isfinite(ref[~nan_rows]))
+    for splits in (None, 3):
+        say("decode: non-finite query elements, splits=%s" % splits)
+        if splits is None:
+            out = kv8.absorb_decode(ql_d, qr_d, codes, scales, st, ln, w.max_len, w.softmax_scale)
+        else:
+            out = kv8.absorb_decode_splitT(ql_d, qr_d, codes, scales, st, ln, w.max_len,
+                                           w.softmax_scale, splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(w.B, w.H, KL)
+        assert np.all(np.isnan(got[nan_rows]))
+        assert np.all(np.isfinite(got[~nan_rows]))
+        e = rel_err(got[~nan_rows], ref[~nan_rows])
+        say("  max|d|/max|ref| over the finite rows = %.3g" % e)
+        assert e <= TOL, e
+
+
 def _unit(v):
     return v / np.linalg.norm(v, axis=-1, keepdims=True)
 
@@ -226,9 +305,11 @@ def test_cancelling_ranges_within_the_partials_bound(kv8):
     assert 10.0 < ratio < 65.0
 
 
-@pytest.mark.parametrize("T", [96, 3072])
-def test_tile_count_multiple_of_three(kv8, T):
-    """3 and 96 tiles of 32 rows (the last iteration then re-copies into the
+@pytest.mark.parametrize("T", [64, 96, 3072, 3104])
+def test_tile_counts_around_the_buffer_ring(kv8, T):
+    """2, 3, 96 and 97 tiles of 32 rows: every residue of the tile count
+    modulo the four raw tile buffers (the tile loop is unrolled by four; the
+    last iterations re-copy the last tile, and one re-copy goes into the
     buffer the epilogue reuses): the direct output (B=128, H=256: 256 blocks,
     one range each) and the partials of one range merged."""
     w = workloads.tiny(seed=36, B=128, Q=1, H=256, T=T, outlier_p=0.0)

@@ -632,17 +632,21 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // per-lane byte offsets do not depend on the tile.
     // A tile's code rows: one buffer resource (its first row, valid rows x
     // 576 bytes) for all its code copies.
+    // (token offsets inside a range fit 32 bits: kv_len is a 32-bit count)
     struct TileSrc {
-        int64_t t0;
-        int valid;
+        int rel;    // first token of the tile, relative to ts
+        int valid;  // its tokens inside the range (uniform, >= 1)
         i32x4_t rsrc;
     };
+    const uint8_t* const codes_rng = p.codes + (row_base + ts) * kRowBytes;
+    const int ntok32 = static_cast<int>(ntok);
     auto tile_src = [&](int tile) {
         tile = tile < ntiles ? tile : ntiles - 1;
         TileSrc ts_;
-        ts_.t0 = ts + static_cast<int64_t>(tile) * kTT;
-        ts_.valid = static_cast<int>(te - ts_.t0 < kTT ? te - ts_.t0 : kTT);  // (uniform, >= 1)
-        ts_.rsrc = buffer_rsrc(p.codes + (row_base + ts_.t0) * kRowBytes, static_cast<uint32_t>(ts_.valid * kRowBytes));
+        ts_.rel = tile * kTT;
+        ts_.valid = ntok32 - ts_.rel < kTT ? ntok32 - ts_.rel : kTT;
+        ts_.rsrc = buffer_rsrc(codes_rng + static_cast<int64_t>(ts_.rel) * kRowBytes,
+                               static_cast<uint32_t>(ts_.valid * kRowBytes));
         return ts_;
     };
     const uint32_t lc_off = static_cast<uint32_t>(dma_lc(lane) + 32 * w);  // (Lc copy k: source + 128 k)
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
         } else if (w < 2) {
             copy_to_lds_b128_rsrc(src.rsrc, static_cast<uint32_t>(dma_rc(ln)), 0, lds_addr(&s_rc[lbuf][1024 * w]));
         } else if (w == 3) {
-            const int64_t t0 = src.t0;
+            const int64_t t0 = ts + src.rel;
             const int valid = src.valid;
             if constexpr (kMX) {
                 // the tile's 576 exponent bytes, 16 per lane on lanes 0-35; the
@@ -1260,11 +1264,12 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
     // pass) and waited for at the end of iteration i - 2; iteration i runs
     //   phase A: score(i + 1) from its raw codes, with the softmax of tile i
     //            (its scores x were formed last iteration), three copies of
-    //            tile i + 3 and (block-scaled rows) the decode of tile i + 1
-    //            into an fp16 Lc tile between its MFMAs
+    //            tile i + 3 and the decoded scales of tile i + 1 (block-scaled
+    //            rows: its scales in phase B, and the decode of tile i + 1
+    //            into an fp16 Lc tile) between its MFMAs
     //   phase B: context(i) with the P' of that softmax (from tile i's raw
-    //            codes, or its fp16 tile), with the scales and scores x of
-    //            tile i + 1 and two copies of tile i + 3 between its MFMAs
+    //            codes, or its fp16 tile), with the scores x of tile i + 1
+    //            and two copies of tile i + 3 between its MFMAs
     // and one barrier, after the copies of tile i + 2 have landed (those of
     // tile i + 3 stay in flight).  Stages past the last tile run on
     // re-copies of the last tile and their results are never used.
@@ -1333,22 +1338,37 @@ __global__ __launch_bounds__(kThreads, 1) void absorb_decode_kernel(DecodeArgs p
                 }
                 if constexpr (st >= 12 && st < 16) scales_load_e(D0, st - 12);
                 decode_step(sc, RN, D1);
+                // per-row scales of tile it + 1 (landed at the last barrier):
+                // decoded here, so that phase B only loads them
+                if constexpr (!kMX && st == 2) decode_scales(RN, D1, it + 1);
                 if constexpr (st == 5 || st == 9 || st == 13)
                     issue_copy(csrc, RC, std::integral_constant<int, (st - 5) / 4>{}, lane);
                 order();
             });
             l_run += lsum;
             // ---------------- phase B: context(it) from buffer CB (written
-            //                  before the last barrier), scales and scores x of
-            //                  tile it + 1
+            //                  before the last barrier), scores x of tile it + 1
             if constexpr (kMX) phase_b_offsets(fresh_lane_id());
             context_begin(CB);
             order();
             static_for<32>([&](auto nc) {
                 constexpr int n = decltype(nc)::value;
                 context_step(CB, n, n < 16 ? pa[0] : pa[1]);
-                if constexpr (n == 0) mfma_acc_drain(accL, accR);
-                if constexpr (n >= 12 && n < 23) scores_step(std::integral_constant<int, n - 12>{}, RN, D1, it + 1);
+                // (the scores x are formed from step 12 on: the score MFMAs of
+                // phase A are more than 18 wait states back by then)
+                if constexpr (kMX && n >= 12 && n < 23)
+                    scores_step(std::integral_constant<int, n - 12>{}, RN, D1, it + 1);
+                if constexpr (!kMX && n >= 12 && n < 20 && n % 2 == 0) {
+                    // the scales of token group (n - 12) / 2, three MFMAs
+                    // before its scores are formed
+                    scales_load_l(D1, (n - 12) / 2);
+                    scales_load_r(D1, (n - 12) / 2);
+                }
+                if constexpr (!kMX && n >= 15 && n < 23 && n % 2 == 1) {
+                    constexpr int q4 = (n - 15) / 2;
+                    form_x(q4);
+                    pin(x[4 * q4]); pin(x[4 * q4 + 1]); pin(x[4 * q4 + 2]); pin(x[4 * q4 + 3]);
+                }
                 if constexpr (n == 5 || n == 25)
                     issue_copy(csrc, RC, std::integral_constant<int, 3 + n / 16>{}, lane);
                 order();

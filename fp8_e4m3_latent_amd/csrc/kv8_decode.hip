@@ -1643,16 +1643,32 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const int16_t*
     const int grp = tid >> 5, q = tid & 31;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lsum > 0.0f) {
+        // group grp sums the ranges grp, grp + 8, ... in that order, eight of
+        // them loaded at once (indices past the last range repeat range grp
+        // with weight 0: its codes are finite)
         const int16_t* po = part_o + br * kKvLora + col0 + 4 * q;
-        for (int s = grp; s < n_splits; s += kMergeGroups) {
-            const RangeStat st = part_ml[s * stride + br];
-            const uint2 o = *reinterpret_cast<const uint2*>(po + static_cast<int64_t>(s) * stride * kKvLora);
-            const float ws = range_weight(st, cpos, cabs, kmax) * st.l * inv_l * st.o_scale;
-            const float4 v = codes4_to_f32(o);
-            acc.x += ws * v.x;
-            acc.y += ws * v.y;
-            acc.z += ws * v.z;
-            acc.w += ws * v.w;
+        for (int s0 = grp; s0 < n_splits; s0 += 8 * kMergeGroups) {
+            RangeStat st8[8];
+            uint2 o8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = s0 + u * kMergeGroups;
+                const int sc = s < n_splits ? s : grp;
+                st8[u] = part_ml[sc * stride + br];
+                o8[u] = *reinterpret_cast<const uint2*>(po + static_cast<int64_t>(sc) * stride * kKvLora);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const RangeStat st = st8[u];
+                const float ws = s0 + u * kMergeGroups < n_splits
+                                     ? range_weight(st, cpos, cabs, kmax) * st.l * inv_l * st.o_scale
+                                     : 0.0f;
+                const float4 v = codes4_to_f32(o8[u]);
+                acc.x += ws * v.x;
+                acc.y += ws * v.y;
+                acc.z += ws * v.z;
+                acc.w += ws * v.w;
+            }
         }
     }
     s_acc[grp][q] = acc;

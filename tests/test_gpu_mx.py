@@ -127,6 +127,38 @@ def test_decode_ragged_causal_and_empty(kv8):
     assert not got[0].any() and not got[1, :2].any()
 
 
+def test_decode_query_rows_of_any_magnitude(kv8):
+    """Query rows scaled by 1e-37 … 1e36 over block-scaled rows scaled by the
+    inverse (softmax scale 1, scores spread over several natural-log units),
+    and query elements spread over 2^-40..1: the two e4m3 query terms of the
+    scaled score MFMAs reproduce the bf16 queries (the same terms as the
+    per-row path)."""
+    T = 300
+    mq = np.array([1e-37, 1e-30, 1e20, 1e36, 1.0])
+    B = len(mq)
+    w = workloads.tiny(seed=85, B=B, Q=1, H=32, T=T, outlier_p=0.0)
+    ql = workloads.bf16_to_f32(w.q_lat).astype(np.float64)
+    qr = workloads.bf16_to_f32(w.q_rope).astype(np.float64)
+    rng = np.random.default_rng(86)
+    for b in range(B):
+        if b == B - 1:
+            ql[b] = np.copysign(np.exp2(rng.uniform(-40.0, 0.0, size=ql[b].shape)), ql[b])
+            qr[b] = np.copysign(np.exp2(rng.uniform(-40.0, 0.0, size=qr[b].shape)), qr[b])
+            mr = 0.5
+        else:
+            ql[b] *= mq[b]
+            qr[b] *= mq[b]
+            mr = 3.0 / mq[b]
+        w.rows[b * T:(b + 1) * T] *= np.float32(mr)
+    w.q_lat = workloads.bf16_bits(ql.astype(np.float32))
+    w.q_rope = workloads.bf16_bits(qr.astype(np.float32))
+    assert np.all(np.isfinite(w.rows))
+    w.softmax_scale = np.float32(1.0)
+    cache = mx_cache(kv8, w.rows)
+    run_case(kv8, w, cache=cache)
+    run_case(kv8, w, splits=2, cache=cache)
+
+
 def test_decode_rows_with_widely_spread_block_scales(kv8):
     """Blocks of one row 2^-40 .. 2^40 apart, rows of magnitude 1e-25 .. 1e20
     (every value finite in f32)."""

@@ -1707,17 +1707,20 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_rows_kernel
     const float wsc = lsum > 0.0f ? wgt * st.l * (1.0f / lsum) * st.o_scale : 0.0f;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
     const int16_t* po = part_o + br * kKvLora + 8 * lane;
-    // eight ranges' codes loaded at once, without branches: the codes of an
-    // empty range are not written, but any int16 value is finite, so its zero
-    // weight adds exactly 0; indices past the last range repeat it with
-    // weight 0
-    for (int s2 = 0; s2 < n_splits; s2 += 8) {
+    // Only ranges up to the last one that saw a token are read (the ranges
+    // past a sequence's end are empty).  Eight ranges' codes are loaded at
+    // once, without branches: the codes of an empty range are not written,
+    // but any int16 value is finite, so its zero weight adds exactly 0;
+    // indices past the last live range repeat it with weight 0.
+    const uint64_t live = __ballot(st.l != 0.0f);  // (NaN sums count as live)
+    const int n_live = live != 0 ? 64 - __clzll(static_cast<long long>(live)) : 0;
+    for (int s2 = 0; s2 < n_live; s2 += 8) {
         uint4 o8[8];
         float w8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int su = s2 + u < n_splits ? s2 + u : n_splits - 1;
-            w8[u] = s2 + u < n_splits ? __shfl(wsc, su, 64) : 0.0f;
+            const int su = s2 + u < n_live ? s2 + u : n_live - 1;
+            w8[u] = s2 + u < n_live ? __shfl(wsc, su, 64) : 0.0f;
             o8[u] = *reinterpret_cast<const uint4*>(po + static_cast<int64_t>(su) * stride * kKvLora);
         }
 #pragma unroll

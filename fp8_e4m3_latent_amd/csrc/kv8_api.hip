@@ -1,17 +1,52 @@
 // C ABI of libkv8 (declared in include/kv8.h): argument checks and launches.
-// No call allocates except kv8_absorb_decode's stream-ordered split partials,
-// none synchronizes the host, none prints or aborts.
+// No call allocates except kv8_absorb_decode's stream-ordered split partials
+// (from a pool of the library's own), none synchronizes the host, none prints
+// or aborts.
 #include "kv8.h"
 
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
+#include <mutex>
 
 #include "kv8_internal.hpp"
 
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kPoolDevices = 64;
+
+// The stream-ordered memory pool of the current device from which
+// kv8_absorb_decode takes its split partials (created on the first call on
+// the device), or nullptr on failure.  Its release threshold keeps the memory
+// a call frees in the pool, so the next call reuses it instead of asking the
+// driver again; the pool holds the largest partials in use at once until the
+// process ends.
+hipMemPool_t partials_pool() {
+    static std::mutex mu;
+    static hipMemPool_t pools[kPoolDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kPoolDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (pools[dev] == nullptr) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess || pool == nullptr) return nullptr;
+        uint64_t keep = UINT64_MAX;
+        if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return nullptr;
+        }
+        pools[dev] = pool;
+    }
+    return pools[dev];
+}
 
 int launched(int rc) { return rc == 0 ? KV8_OK : KV8_ELAUNCH; }
 
@@ -292,7 +327,9 @@ int kv8_absorb_decode(const uint16_t* q_lat, const uint16_t* q_rope, const uint8
     d.n_splits = splits;
     d.split_chunk = chunk;
     const size_t bytes = kv8::splitT_workspace_bytes(B, Q, H, d.n_splits);
-    if (hipMallocAsync(&d.workspace, bytes, st) != hipSuccess) return KV8_ENOMEM;
+    hipMemPool_t pool = partials_pool();
+    if (pool == nullptr || hipMallocFromPoolAsync(&d.workspace, bytes, pool, st) != hipSuccess)
+        return KV8_ENOMEM;
     rc = launched(kv8::launch_absorb_decode(d, st));
     if (hipFreeAsync(d.workspace, st) != hipSuccess && rc == KV8_OK) rc = KV8_ELAUNCH;
     return rc;

@@ -32,12 +32,15 @@
  *   - `stream` is a hipStream_t (NULL = the default stream); calls are
  *     asynchronous on it and never synchronize the host;
  *   - bf16 values are passed as their uint16_t bit patterns;
- *   - the library keeps no state between calls.  One call allocates:
- *     kv8_absorb_decode takes stream-ordered device memory (hipMallocAsync)
- *     for its split partials and returns it on the same stream before
- *     returning (its signature has no workspace).  Every other call runs on
- *     caller memory only; kv8_absorb_decode_splitT and the two-stage form are
- *     the allocation-free decode calls;
+ *   - the kernel calls keep no results between calls.  One call allocates:
+ *     kv8_absorb_decode takes stream-ordered device memory for its split
+ *     partials from a memory pool of the library's own (one per device,
+ *     created on the first such call on it) and returns it to that pool on
+ *     the same stream before returning (its signature has no workspace); the
+ *     pool keeps that memory for later calls until the process ends.  Every
+ *     other call runs on caller memory only; kv8_absorb_decode_splitT, the
+ *     two-stage form and kv8_absorb_decode_noalloc are the allocation-free
+ *     decode calls;
  *   - argument errors are reported synchronously through the return value
  *     and nothing is launched; data is never an error (NaN, inf, zero and
  *     subnormal values have defined results); nothing aborts or prints.

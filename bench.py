@@ -710,7 +710,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "e4m3+f16",  # score MFMAs on e4m3 operands, context MFMAs on f16, f32 sums
         "data": "synthetic",
         "config": {"workload": "batched absorbed-MLA decode step: B=32 x T=8192 x H=128, Q=1, "
                                "latent 512+64 e4m3 with per-row f32 scales; append 1 row/sequence "

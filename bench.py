@@ -399,7 +399,31 @@ def leg_quantize(torch, kv8, W, steps):
     return res
 
 
-def _decode_workload_leg(torch, kv8, w, steps, splits=None, cpu_sel=None, cpu_what=""):
+def long_context_stats(torch, w, codes, scales, ql, qr):
+    """The softmax of the long-context workload over its dequantized cache, in
+    f32 with plain torch on the device (a property of the workload, not a
+    measurement of the kernels): per head, the largest weight and the weight
+    on the head's own planted rows."""
+    x = codes.view(torch.float8_e4m3fn).to(torch.float32)
+    s = (ql.float().reshape(-1, KL) @ (x[:, :KL] * scales[:, :1]).T.contiguous()
+         + qr.float().reshape(-1, KR) @ (x[:, KL:] * scales[:, 1:2]).T.contiguous())
+    del x
+    p = torch.softmax(s * float(w.softmax_scale), dim=1)
+    del s
+    pos = torch.from_numpy(w.notes["planted_rows"]).to(p.device)
+    heads = torch.from_numpy(w.notes["planted_heads"]).to(p.device)
+    mass = torch.zeros(w.H, dtype=torch.float64, device=p.device)
+    mass.index_add_(0, heads, p[heads, pos].double())
+    maxp = p.max(dim=1).values.double()
+    q = lambda t: [float(t.min()), float(t.median()), float(t.max())]
+    return {"what": "per head (min, median, max over the %d heads), softmax over the dequantized "
+                    "cache; planted_mass is the weight on the head's own planted rows" % w.H,
+            "planted_rows": int(len(w.notes["planted_rows"])),
+            "max_p": q(maxp), "planted_mass": q(mass)}
+
+
+def _decode_workload_leg(torch, kv8, w, steps, splits=None, cpu_sel=None, cpu_what="",
+                         stats=None):
     dev = "cuda"
     rows = torch.from_numpy(w.rows).to(dev)
     n = w.n_rows
@@ -436,6 +460,8 @@ def _decode_workload_leg(torch, kv8, w, steps, splits=None, cpu_sel=None, cpu_wh
            "kv_gb_per_s": kv_bytes / (ms * 1e-3) / 1e9,
            "cache_build": {"rows": n, **qst, "rows_per_s": n / (qt * 1e-3),
                            "gb_per_s": qbytes / (qt * 1e-3) / 1e9}}
+    if stats is not None:
+        res["workload_stats"] = stats(torch, w, codes, scales, ql, qr)
     if cpu_sel is not None:
         import oracle
         log("cpu baseline: %s" % cpu_what)
@@ -682,7 +708,8 @@ def main():
         sel = np.arange(0, 128, 8) if cpu_on else None
         extra["splitT_256k"] = _decode_workload_leg(
             torch, kv8, W.long_context(seed=0), max(5, args.steps // 2), splits=64, cpu_sel=sel,
-            cpu_what="256k-token slot, every 8th of the 128 heads (16 rows), T=262,144")
+            cpu_what="256k-token slot, every 8th of the 128 heads (16 rows), T=262,144",
+            stats=long_context_stats)
     if "project" in legs:
         log("project: 8192 rows x N=32768")
         extra["project_8k"] = leg_project(torch, kv8, max(5, args.steps // 4))

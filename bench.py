@@ -325,8 +325,9 @@ def cpu_quantize_baseline(W, cores):
         x = np.ascontiguousarray(rows_h[:n])
         dt, times = _oracle_passes(lambda: oracle.quantize_rows(x, threads=threads), 3.0)
         key = "value" if threads == cores else "threads_1"
-        rec = {"value": n / dt, "sample": "%d Student-t bulk rows (8,192 tokens x 8 layers, special "
-                                           "rows planted), median of %d passes" % (n, len(times))}
+        rec = {"value": n / dt, "gb_per_s": n * 2888 / dt / 1e9,  # 2,888 algorithmic bytes a row
+               "sample": "%d Student-t bulk rows (8,192 tokens x 8 layers, special "
+                         "rows planted), median of %d passes" % (n, len(times))}
         if threads == cores:
             out.update(rec)
         else:

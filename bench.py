@@ -416,7 +416,7 @@ def long_context_stats(torch, w, codes, scales, ql, qr):
     mass = torch.zeros(w.H, dtype=torch.float64, device=p.device)
     mass.index_add_(0, heads, p[heads, pos].double())
     maxp = p.max(dim=1).values.double()
-    q = lambda t: [float(t.min()), float(t.median()), float(t.max())]
+    q = lambda t: [float(t.min()), float(t.quantile(0.5)), float(t.max())]
     return {"what": "per head (min, median, max over the %d heads), softmax over the dequantized "
                     "cache; planted_mass is the weight on the head's own planted rows" % w.H,
             "planted_rows": int(len(w.notes["planted_rows"])),
